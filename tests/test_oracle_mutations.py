@@ -1,0 +1,75 @@
+"""Mistakes planted in copies of the oracle (on the CPU) must each fail at
+least one pin in test_oracle_pins.py.  This shows the pins constrain the
+oracle rather than restate it."""
+import inspect
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+from conftest import load_golden
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTATIONS = {
+    "scale dropped": ("s[j] = scale * dot;", "s[j] = dot;"),
+    "causal excludes the diagonal": ("(j) <= causal_i))", "(j) < causal_i))"),
+    "causal reversed": ("(j) <= causal_i))", "(j) >= causal_i))"),
+    "no max shift": ("s[j] = exp(s[j] - m);", "s[j] = exp(s[j]);"),
+    "lse without max": ("if (lse) *lse = m + log(Z);", "if (lse) *lse = log(Z);"),
+    "weights not normalised": ("double w = s[j] / Z;", "double w = s[j];"),
+    "key padding ignored": ("if (c->seqlens_kv && c->seqlens_kv[b] < legal_end) legal_end = c->seqlens_kv[b];\n"
+                            "    const double* q = c->q",
+                            "const double* q = c->q"),
+    "query padding ignored": ("if (c->seqlens_q && i >= c->seqlens_q[b]) {       /* padded query row */",
+                              "if (0) {"),
+    "heads interleaved in Q": ("const double* q = c->qp + r * wq + (int64_t)h * c->d_k;",
+                               "const double* q = c->qp + r * wq + (int64_t)h;"),
+    "concat order reversed": ("ocat + (int64_t)h * c->d_v, NULL);",
+                              "ocat + (int64_t)(c->H - 1 - h) * c->d_v, NULL);"),
+    "value row shifted": ("const double* vj = V + (int64_t)j * v_stride;",
+                          "const double* vj = V + (int64_t)(j == 0 ? 0 : j - 1) * v_stride;"),
+}
+
+
+def _pin_functions():
+    out = []
+    for name, fn in inspect.getmembers(pins, inspect.isfunction):
+        if not name.startswith("test_"):
+            continue
+        params = inspect.signature(fn).parameters
+        if "causal" in params:
+            out += [(f"{name}[{c}]", fn, {"causal": c}) for c in (False, True)]
+        elif "golden" in params:
+            out.append((name, fn, {"golden": load_golden}))
+        else:
+            out.append((name, fn, {}))
+    return out
+
+
+@pytest.mark.parametrize("mutation", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(mutation, tmp_path):
+    old, new = MUTATIONS[mutation]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, "mutation anchor not found"
+    mutated = tmp_path / "oracle_mut.c"
+    mutated.write_text(src.replace(old, new))
+    so = tmp_path / "liboracle_mut.so"
+    subprocess.check_call(["gcc", "-O1", "-fPIC", "-shared", "-pthread", "-o", str(so), str(mutated), "-lm"])
+    saved_path, saved_lib = oracle._LIB_PATH, oracle._lib
+    try:
+        oracle._lib = None
+        oracle._LIB_PATH = str(so)
+        oracle._SRC = str(mutated)
+        oracle._load()
+        failed = []
+        for name, fn, kw in _pin_functions():
+            try:
+                fn(**kw)
+            except Exception:  # an assertion or a NaN-triggered error both count
+                failed.append(name)
+        assert failed, f"no pin caught the planted mistake: {mutation}"
+    finally:
+        oracle._lib, oracle._LIB_PATH, oracle._SRC = saved_lib, saved_path, SRC

@@ -1,0 +1,333 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test names the fact it pins and the plausible oracle mistake it would
+catch (wrong or missing scale, transposed operands, softmax over the wrong
+axis, off-by-one or reversed causal mask, padding applied to the wrong side,
+mixed-up head slicing, wrong weight orientation, wrong log-sum-exp).
+Runs on the CPU only.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import attn_inputs as gen
+import oracle
+
+
+def rnd(seed, shape):
+    return gen.normal(seed, shape)
+
+
+def weights_via_identity(q, k, **kw):
+    """Attention weights P: with V = I (d_v = n_kv) the output row is the
+    weight row."""
+    B, H, n_q, _ = q.shape
+    n_kv = k.shape[2]
+    eye = np.broadcast_to(np.eye(n_kv), (B, H, n_kv, n_kv)).copy()
+    o, lse = oracle.sdpa(q, k, eye, **kw)
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Worked examples printed on the pages
+# ---------------------------------------------------------------------------
+def test_p1_two_token_example(golden):
+    """attention-paper-guide section 03.2: 2 tokens, d_k = 2.  Closed form:
+    row 0 scores (1,1)/sqrt2 -> weights (1/2, 1/2); row 1 scores (0,1)/sqrt2 ->
+    weights (1, e^{1/sqrt2}) / (1 + e^{1/sqrt2}).  Catches a missing or wrong
+    scale, Q/K swapped (K Q^T gives different rows), softmax on the wrong axis."""
+    g = golden("p1_two_token_example.txt")
+    Q, K, V = (g[n][None, None] for n in ("Q", "K", "V"))
+    e = math.exp(1 / math.sqrt(2))
+    w_exact = np.array([[0.5, 0.5], [1 / (1 + e), e / (1 + e)]])
+    o_exact = w_exact @ np.array([[10.0, 0.0], [0.0, 6.0]])
+    P, lse = weights_via_identity(Q, K)
+    assert np.abs(P[0, 0] - w_exact).max() < 1e-12
+    o, lse2 = oracle.sdpa(Q, K, V)
+    assert np.abs(o[0, 0] - o_exact).max() < 1e-12
+    # the page's printed values, to its printed precision
+    assert np.abs(P[0, 0] - g["weights_printed"]).max() <= 0.005 + 1e-12
+    assert np.abs(o[0, 0] - g["output_printed"]).max() <= 0.05
+    assert abs(o[0, 0, 1, 1] - 4.02) <= 0.005  # the page's two-decimal value
+    # log-sum-exp closed form: ln(2 e^{1/sqrt2}) and ln(1 + e^{1/sqrt2})
+    lse_exact = [1 / math.sqrt(2) + math.log(2), math.log(1 + e)]
+    assert np.abs(lse2[0, 0] - lse_exact).max() < 1e-12
+    # causal: row 0 may only see key 0, so it equals V[0] exactly
+    oc, _ = oracle.sdpa(Q, K, V, causal=True)
+    assert np.array_equal(oc[0, 0, 0], [10.0, 0.0])
+    assert np.abs(oc[0, 0, 1] - o_exact[1]).max() < 1e-12
+
+
+def test_p4_ledger_from_printed_qkv(golden):
+    """rockcohen.cc section 5.1 ledger: S = QK^T/sqrt2, A = softmax(S), z0;
+    section 5.3 causal rows.  S is recovered from the oracle's outputs as
+    log(A) + lse, so this also pins the log-sum-exp."""
+    g = golden("p4_running_example_ledger.txt")
+    Q, K, V = (g[n][None, None] for n in ("Q", "K", "V"))
+    A, lse = weights_via_identity(Q, K)
+    assert np.abs(A[0, 0] - g["A"]).max() < 2e-3
+    S = np.log(A[0, 0]) + lse[0, 0][:, None]
+    assert np.abs(S - g["S"]).max() < 2e-3
+    o, _ = oracle.sdpa(Q, K, V)
+    assert np.abs(o[0, 0, 0] - g["z0"][0]).max() < 2e-3
+    Ac, _ = weights_via_identity(Q, K, causal=True)
+    assert np.abs(Ac[0, 0, :2] - g["causal_rows_0_1"]).max() < 2e-3
+    assert np.all(Ac[0, 0][np.triu_indices(4, 1)] == 0.0)
+
+
+def test_p4_ledger_through_mha(golden):
+    """The same ledger through the multi-head path with one head: projections
+    X.W^Q, X.W^K, X.W^V (the page's orientation, W in R^{4x2}), then W^O that
+    keeps the two attention columns.  Catches a transposed weight or a wrong
+    projection operand."""
+    g = golden("p4_running_example_ledger.txt")
+    X = g["X"][None]
+    WO = np.zeros((2, 4))
+    WO[0, 0] = WO[1, 1] = 1.0
+    y = oracle.mha(X, X, g["WQ"], g["WK"], g["WV"], WO, heads=1)
+    assert np.abs(y[0, 0, :2] - g["z0"][0]).max() < 2e-3
+    assert np.all(y[0, :, 2:] == 0.0)
+    # the whole Z agrees with A.V from the printed ledger
+    Z = g["A"] @ g["V"]
+    assert np.abs(y[0, :, :2] - Z).max() < 2e-3
+    # causal rows through the block (row 0 = V[0] of the projections)
+    yc = oracle.mha(X, X, g["WQ"], g["WK"], g["WV"], WO, heads=1, causal=True)
+    assert np.abs(yc[0, 0, :2] - (g["X"] @ g["WV"])[0]).max() < 1e-15
+
+
+# ---------------------------------------------------------------------------
+# Definition-level invariants (rockcohen.cc section 10.2, P0 and P1)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_sum_to_one(causal):
+    B, H, n_q, n_kv, d = 2, 3, 37, 37, 16
+    q, k = rnd(1, (B, H, n_q, d)), rnd(2, (B, H, n_kv, d))
+    lkv = np.array([37, 5], np.int32)
+    v = np.ones((B, H, n_kv, 3))
+    o, _ = oracle.sdpa(q, k, v, causal=causal, seqlens_kv=lkv)
+    assert np.abs(o - 1.0).max() < 1e-12
+    P, _ = weights_via_identity(q, k, causal=causal, seqlens_kv=lkv)
+    assert np.all(P >= 0)
+
+
+def test_causal_upper_triangle_exact_zero_and_row0():
+    """rockcohen.cc section 6.3: -inf at the softmax input gives weights that
+    are exactly 0.0 for future keys; row 0 sees only key 0."""
+    q, k = rnd(3, (1, 2, 20, 8)), rnd(4, (1, 2, 20, 8))
+    P, _ = weights_via_identity(q, k, causal=True)
+    iu = np.triu_indices(20, 1)
+    assert np.all(P[:, :, iu[0], iu[1]] == 0.0)
+    assert np.all(P[:, :, np.arange(20), np.arange(20)] > 0)  # diagonal is legal
+    v = rnd(5, (1, 2, 20, 8))
+    o, _ = oracle.sdpa(q, k, v, causal=True)
+    assert np.array_equal(o[:, :, 0], v[:, :, 0])
+
+
+def test_mask_equals_renormalising_over_legal_keys():
+    """rockcohen.cc section 6.3: masking at the input equals a softmax over the
+    legal set.  Causal row i == unmasked attention over keys 0..i; key padding
+    == attention on the truncated K/V; padding is on keys, not queries."""
+    q, k, v = rnd(6, (1, 1, 12, 8)), rnd(7, (1, 1, 12, 8)), rnd(8, (1, 1, 12, 5))
+    oc, lc = oracle.sdpa(q, k, v, causal=True)
+    for i in range(12):
+        oi, li = oracle.sdpa(q[:, :, i:i + 1], k[:, :, :i + 1], v[:, :, :i + 1])
+        assert np.abs(oc[0, 0, i] - oi[0, 0, 0]).max() < 1e-14
+        assert abs(lc[0, 0, i] - li[0, 0, 0]) < 1e-14
+    L = np.array([7], np.int32)
+    kp, vp = k.copy(), v.copy()
+    kp[:, :, 7:] = np.nan
+    vp[:, :, 7:] = np.nan  # padding must never be read
+    op, _ = oracle.sdpa(q, kp, vp, seqlens_kv=L)
+    ot, _ = oracle.sdpa(q, k[:, :, :7], v[:, :, :7])
+    assert np.abs(op - ot).max() < 1e-14
+    # query lengths: rows past L_q are zero, the rest unchanged
+    oq, lq = oracle.sdpa(q, k, v, seqlens_q=L)
+    of, _ = oracle.sdpa(q, k, v)
+    assert np.all(oq[:, :, 7:] == 0.0) and np.all(np.isneginf(lq[:, :, 7:]))
+    assert np.array_equal(oq[:, :, :7], of[:, :, :7])
+
+
+def test_empty_key_set_gives_zero_row():
+    q, k, v = rnd(9, (2, 1, 4, 8)), rnd(10, (2, 1, 6, 8)), rnd(11, (2, 1, 6, 8))
+    L = np.array([0, 6], np.int32)
+    o, lse = oracle.sdpa(q, k, v, seqlens_kv=L)
+    assert np.all(o[0] == 0.0) and np.all(np.isneginf(lse[0]))
+    assert np.all(np.isfinite(o[1]))
+
+
+def test_permutation_equivariance_and_key_invariance():
+    """rockcohen.cc sections 3.4 and 6.2 (P1): without a mask,
+    f(PQ, PK, PV) = P f(Q, K, V), and permuting keys with their values changes
+    nothing."""
+    q, k, v = rnd(12, (1, 2, 9, 8)), rnd(13, (1, 2, 9, 8)), rnd(14, (1, 2, 9, 8))
+    perm = np.random.default_rng(0).permutation(9)
+    o, _ = oracle.sdpa(q, k, v)
+    op, _ = oracle.sdpa(q[:, :, perm], k[:, :, perm], v[:, :, perm])
+    assert np.abs(op - o[:, :, perm]).max() < 1e-12
+    ok, _ = oracle.sdpa(q, k[:, :, perm], v[:, :, perm])
+    assert np.abs(ok - o).max() < 1e-12
+
+
+def test_shift_invariance_and_overflow_safety():
+    """rockcohen.cc section 3.2: adding a constant to a row of scores leaves the
+    weights unchanged.  K_j + u for all j adds q.u to every score of row q.
+    A large u (scores near +1e3) checks the max subtraction."""
+    q, k, v = rnd(15, (1, 1, 10, 8)), rnd(16, (1, 1, 10, 8)), rnd(17, (1, 1, 10, 4))
+    o, _ = oracle.sdpa(q, k, v)
+    u = rnd(18, (8,))
+    o1, _ = oracle.sdpa(q, k + u, v)
+    assert np.abs(o1 - o).max() < 1e-12
+    q2 = np.abs(q) + 1.0
+    u_big = np.full(8, 400.0)  # q.u >= 3200 scaled by 1/sqrt(8): ~1e3
+    o2, _ = oracle.sdpa(q2, k, v)
+    o3, _ = oracle.sdpa(q2, k + u_big, v)
+    assert np.all(np.isfinite(o3)) and np.abs(o3 - o2).max() < 1e-9
+
+
+def test_scale_brings_score_variance_to_one():
+    """vlmlib.cn summary / rockcohen.cc section 5.1 (paper footnote 4): for
+    iid N(0,1) components, q.k has variance d_k; dividing by sqrt(d_k) brings
+    it to 1.  Scores are recovered as log(P) + lse."""
+    d = 64
+    q, k = rnd(19, (1, 4, 64, d)), rnd(20, (1, 4, 64, d))
+    P, lse = weights_via_identity(q, k)
+    S = np.log(P) + lse[..., None]
+    assert abs(S.var() - 1.0) < 0.1
+    raw = q @ np.swapaxes(k, -1, -2)
+    assert abs(np.abs(S * math.sqrt(d) - raw).max()) < 1e-10
+
+
+def test_special_cases():
+    q, k, v = rnd(21, (1, 1, 5, 8)), rnd(22, (1, 1, 7, 8)), rnd(23, (1, 1, 7, 6))
+    # one key: the output is that value row
+    o, _ = oracle.sdpa(q, k[:, :, :1], v[:, :, :1])
+    assert np.array_equal(o, np.broadcast_to(v[:, :, :1], o.shape))
+    # all-zero keys: uniform weights -> mean of the value rows
+    o, _ = oracle.sdpa(q, np.zeros_like(k), v)
+    assert np.abs(o - v.mean(axis=2, keepdims=True)).max() < 1e-14
+    # value columns are independent: a column subset of V gives that subset of O
+    o, _ = oracle.sdpa(q, k, v)
+    o2, _ = oracle.sdpa(q, k, v[..., [1, 4]])
+    assert np.array_equal(o2, o[..., [1, 4]])
+    # huge scale -> softmax tends to argmax: output is the argmax row of V
+    o, _ = oracle.sdpa(q, k, v, scale=1e6)
+    idx = np.argmax(q[0, 0] @ k[0, 0].T, axis=1)
+    assert np.abs(o[0, 0] - v[0, 0, idx]).max() < 1e-12
+
+
+def test_bf16_storage_rounding_matches_torch():
+    """Both roundings (generator's and the oracle's storage diagnostic) agree
+    with torch's float32 -> bfloat16 conversion (round to nearest even)."""
+    import torch
+    x = gen.normal(24, (4096,)) * np.exp(gen.normal(25, (4096,)) * 4)
+    x32 = x.astype(np.float32).astype(np.float64)  # values torch sees exactly
+    ref = torch.tensor(x32, dtype=torch.float32).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(gen.round_to_bf16(x32), ref)
+    assert np.array_equal(np.array([oracle.round_bf16(t) for t in x32[:512]]), ref[:512])
+    ties = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8)])
+    assert list(gen.round_to_bf16(ties)) == [1.0, 1 + 2 ** -6, -1.0]
+
+
+def test_thread_count_independence():
+    q, k, v = rnd(26, (2, 3, 33, 16)), rnd(27, (2, 3, 41, 16)), rnd(28, (2, 3, 41, 16))
+    a, la = oracle.sdpa(q, k, v, causal=True, nthreads=1)
+    b, lb = oracle.sdpa(q, k, v, causal=True, nthreads=7)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_rows_api_matches_full():
+    q, k, v = rnd(29, (2, 3, 20, 8)), rnd(30, (2, 3, 25, 8)), rnd(31, (2, 3, 25, 8))
+    L = np.array([25, 11], np.int32)
+    o, lse = oracle.sdpa(q, k, v, causal=True, seqlens_kv=L)
+    rows = np.array([0, 7, 19, 60, 101, 119])
+    orr, lr = oracle.sdpa_rows(q, k, v, rows, causal=True, seqlens_kv=L)
+    assert np.array_equal(orr, o.reshape(-1, 8)[rows])
+    assert np.array_equal(lr, lse.reshape(-1)[rows])
+
+
+# ---------------------------------------------------------------------------
+# Multi-head attention (vlmlib.cn summary; rockcohen.cc section 5.2)
+# ---------------------------------------------------------------------------
+def _mha_case(seed, B=2, n_q=9, n_kv=11, dm=12, h=3):
+    xq, xkv = rnd(seed, (B, n_q, dm)), rnd(seed + 1, (B, n_kv, dm))
+    ws = [rnd(seed + 2 + t, (dm, dm)) * 0.3 for t in range(4)]
+    return xq, xkv, ws, h
+
+
+def test_mha_single_head_is_full_width_sdpa():
+    """h = 1: MultiHead = Attention(XW^Q, XW^K, XW^V) W^O with scale
+    1/sqrt(d_model) (projections by numpy matmul, Y = X.W)."""
+    xq, xkv, (wq, wk, wv, wo), _ = _mha_case(40)
+    y = oracle.mha(xq, xkv, wq, wk, wv, wo, heads=1, causal=False)
+    o, _ = oracle.sdpa((xq @ wq)[:, None], (xkv @ wk)[:, None], (xkv @ wv)[:, None])
+    assert np.abs(y - o[:, 0] @ wo).max() < 1e-12
+
+
+def test_mha_concat_of_heads_on_column_slices():
+    """With W^O = I the block output is Concat(head_1..head_h), head i using the
+    contiguous columns [i*d_k, (i+1)*d_k) of each projection."""
+    xq, xkv, (wq, wk, wv, wo), h = _mha_case(50)
+    dm = wq.shape[0]
+    dk = dm // h
+    y = oracle.mha(xq, xkv, wq, wk, wv, np.eye(dm), heads=h, causal=True)
+    for i in range(h):
+        sl = slice(i * dk, (i + 1) * dk)
+        o, _ = oracle.sdpa((xq @ wq[:, sl])[:, None], (xkv @ wk[:, sl])[:, None],
+                           (xkv @ wv[:, sl])[:, None], causal=True)
+        assert np.abs(y[:, :, sl] - o[:, 0]).max() < 1e-12
+    # general W^O: Y = Concat . W^O
+    y2 = oracle.mha(xq, xkv, wq, wk, wv, wo, heads=h, causal=True)
+    assert np.abs(y2 - y @ wo).max() < 1e-12
+
+
+def test_mha_head_isolation():
+    """Perturbing head i's W^Q columns changes only head i's concat columns."""
+    xq, xkv, (wq, wk, wv, _), h = _mha_case(60)
+    dm = wq.shape[0]
+    dk = dm // h
+    y = oracle.mha(xq, xkv, wq, wk, wv, np.eye(dm), heads=h)
+    wq2 = wq.copy()
+    wq2[:, dk:2 * dk] += 0.5
+    y2 = oracle.mha(xq, xkv, wq2, wk, wv, np.eye(dm), heads=h)
+    changed = np.abs(y2 - y).max(axis=(0, 1)) > 0
+    assert not changed[:dk].any() and changed[dk:2 * dk].all() and not changed[2 * dk:].any()
+
+
+def test_mha_is_not_a_column_split_single_head():
+    """rockcohen.cc section 5.2 / P5: per-head softmax and scale make the
+    multi-head output differ from one full-width head."""
+    xq, xkv, (wq, wk, wv, wo), _ = _mha_case(70, h=2)
+    y1 = oracle.mha(xq, xkv, wq, wk, wv, wo, heads=1)
+    y2 = oracle.mha(xq, xkv, wq, wk, wv, wo, heads=2)
+    assert np.abs(y2 - y1).max() > 1e-3
+
+
+def test_mha_self_attention_permutation_equivariance():
+    """No mask, no positional encoding: f(PX) = P f(X) (rockcohen.cc 6.2)."""
+    xq, _, (wq, wk, wv, wo), h = _mha_case(80)
+    perm = np.random.default_rng(1).permutation(xq.shape[1])
+    y = oracle.mha(xq, xq, wq, wk, wv, wo, heads=h)
+    yp = oracle.mha(xq[:, perm], xq[:, perm], wq, wk, wv, wo, heads=h)
+    assert np.abs(yp - y[:, perm]).max() < 1e-12
+
+
+def test_mha_rows_and_lengths():
+    xq, xkv, (wq, wk, wv, wo), h = _mha_case(90)
+    Lq, Lkv = np.array([9, 4], np.int32), np.array([3, 11], np.int32)
+    y = oracle.mha(xq, xkv, wq, wk, wv, wo, heads=h, seqlens_q=Lq, seqlens_kv=Lkv)
+    assert np.all(y[1, 4:] == 0.0)
+    rows = np.array([0, 5, 8, 9, 12, 17])
+    yr = oracle.mha_rows(xq, xkv, wq, wk, wv, wo, heads=h, rows=rows, seqlens_q=Lq, seqlens_kv=Lkv)
+    assert np.array_equal(yr, y.reshape(-1, y.shape[-1])[rows])
+    # key padding on the block = the block on truncated keys
+    yt = oracle.mha(xq[:1], xkv[:1, :3], wq, wk, wv, wo, heads=h)
+    assert np.abs(y[0] - yt[0]).max() < 1e-13
+
+
+def test_mha_bf16_storage_mode_is_close_but_distinct():
+    xq, xkv, (wq, wk, wv, wo), h = _mha_case(100)
+    y = oracle.mha(xq, xkv, wq, wk, wv, wo, heads=h)
+    yr = oracle.mha(xq, xkv, wq, wk, wv, wo, heads=h, bf16_storage=True)
+    d = np.abs(yr - y).max()
+    assert 0 < d < 0.05
