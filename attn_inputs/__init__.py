@@ -106,8 +106,13 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
 
 
 def bf16_bits(x_bf16_exact: np.ndarray) -> np.ndarray:
-    """uint16 storage of values that are already exactly bf16 (NaN -> 0x7FC0)."""
-    f32 = np.asarray(x_bf16_exact, dtype=np.float64).astype(np.float32)
+    """uint16 storage of values that are already exactly bf16 (NaN -> 0x7FC0).
+    Raises if a value is not exactly representable (round it first)."""
+    x = np.asarray(x_bf16_exact, dtype=np.float64)
+    fin = np.isfinite(x)
+    if not np.array_equal(x[fin], round_to_bf16(x[fin])):
+        raise ValueError("bf16_bits: values are not exactly bf16; round them first")
+    f32 = x.astype(np.float32)
     bits = (f32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
     bits[np.isnan(f32)] = 0x7FC0
     return bits

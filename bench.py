@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention forward hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decoder|encoder|cross|block]
+
+A step is one pass of the hot path over one batch of synthetic input that is
+already resident in HBM:
+  decoder (default)  causal self-attention, [32, 8, 256, 64] bf16 (one SDPA launch)
+  encoder            bidirectional, [32, 8, 128, 64], key/query lengths U{16..128}
+  cross              [16, 16, 256 q, 320 kv, 64], key lengths U{160..320}
+  block              multi-head block, X [4, 4096, 1024], h = 16, causal:
+                     QKV GEMM -> SDPA -> W^O GEMM
+Inputs rotate over enough copies to exceed the 256 MB Infinity Cache (cold
+cache), the K timed steps are captured once in a HIP graph and replayed, and
+HIP events on the launch stream bracket the replay.  Rank 0 prints one JSON
+line.  Work is counted algorithmically: 4*d FLOPs per legal (query, key) pair
+(2*d for Q.K^T and 2*d for P.V), 2*M*N*K per GEMM; bytes are Q, K, V read once
+plus O written once over valid rows.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (bf16) + % of MFMA peak, h=8 d_k=64 n=256 causal"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+CACHE_BYTES = 256 << 20       # Infinity Cache
+WORKLOAD_CFG = {"encoder": 2, "decoder": 3, "cross": 4, "block": 5}
+
+
+def legal_pairs(n_q, n_kv, causal, lq=None, lkv=None, batch=1):
+    """Number of legal (query, key) pairs summed over the batch."""
+    total = 0
+    for b in range(batch):
+        Lq = n_q if lq is None else int(lq[b])
+        Lk = n_kv if lkv is None else int(lkv[b])
+        if causal:
+            total += sum(min(i + 1, Lk) for i in range(Lq))
+        else:
+            total += Lq * Lk
+    return total
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "head_attention_sdpa_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel, from the committed rocprofv3
+    counter summary, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+def to_dev(storage, dtype, dev):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(storage).view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(storage, dtype=np.float32).copy()).to(dev)
+
+
+def time_graph(launches, K, W, torch):
+    """Capture K launches in one graph, replay once untimed after W eager warmup
+    steps, then time one replay with events on the capture/launch stream."""
+    for s in range(W):
+        launches(s)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for s in range(K):
+                launches(s)
+    torch.cuda.synchronize()
+    g.replay()  # untimed: graph upload
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    e1.synchronize()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / K, g
+
+
+def time_eager(launches, K, torch):
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for i in range(K):
+        launches(i)
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / K
+
+
+def bench_sdpa(cfg_id, K, W, args):
+    import torch
+    import attn_inputs as gen
+    import head_attention_sdpa_amd as attn
+
+    attn.lib()
+    dev = torch.device("cuda:0")
+    inp = gen.config(cfg_id)
+    B, H, n_q, n_kv, d_k, d_v = inp.shape
+    per_set = sum(a.nbytes for a in (inp.q_st, inp.k_st, inp.v_st)) + B * H * n_q * d_v * 2
+    R = max(1, math.ceil(2 * CACHE_BYTES / per_set)) if not args.hot else 1
+    base = [to_dev(a, inp.dtype, dev) for a in (inp.q_st, inp.k_st, inp.v_st)]
+    sets = [[t.clone() for t in base] for _ in range(R)]
+    outs = [torch.empty((B, H, n_q, d_v), dtype=base[0].dtype, device=dev) for _ in range(R)]
+    lq = None if inp.seqlens_q is None else torch.from_numpy(inp.seqlens_q).to(dev)
+    lkv = None if inp.seqlens_kv is None else torch.from_numpy(inp.seqlens_kv).to(dev)
+    L = attn.lib()
+    import ctypes
+    st = [[attn.attn_strides(*t.stride()[:3]) for t in s + [o]] for s, o in zip(sets, outs)]
+
+    def launch(s):
+        r = s % R
+        q, k, v = sets[r]
+        sq, sk, sv, so = st[r]
+        rc = L.attn_sdpa_fwd(attn.ATTN_BF16, B, H, n_q, n_kv, d_k, d_v, q.data_ptr(), ctypes.byref(sq),
+                             k.data_ptr(), ctypes.byref(sk), v.data_ptr(), ctypes.byref(sv),
+                             outs[r].data_ptr(), ctypes.byref(so), float(inp.scale),
+                             attn.ATTN_MASK_CAUSAL if inp.causal else attn.ATTN_MASK_NONE,
+                             None if lq is None else lq.data_ptr(),
+                             None if lkv is None else lkv.data_ptr(), None,
+                             torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"attn_sdpa_fwd failed: {attn.status_str(rc)}")
+
+    ms, g = time_graph(launch, K, W, torch)
+    # the graph replays must reproduce the eager result bit for bit
+    ref = outs[0].clone()
+    launch(0)
+    torch.cuda.synchronize()
+    if not torch.equal(ref, outs[0]):
+        raise RuntimeError("graph replay and eager launch disagree")
+    ms_eager = time_eager(launch, K, torch)
+
+    pairs = legal_pairs(n_q, n_kv, inp.causal, inp.seqlens_q, inp.seqlens_kv, B) * H
+    flops = pairs * 2 * (d_k + d_v)
+    Lq = inp.seqlens_q if inp.seqlens_q is not None else np.full(B, n_q)
+    Lk = inp.seqlens_kv if inp.seqlens_kv is not None else np.full(B, n_kv)
+    algo_bytes = int(H * 2 * (Lq.sum() * (d_k + d_v) + Lk.sum() * (d_k + d_v)))
+    tflops = flops / (ms * 1e-3) / 1e12
+    achieved_gbs = algo_bytes / (ms * 1e-3) / 1e9
+    workload = {2: "encoder", 3: "decoder", 4: "cross"}[cfg_id]
+    traffic = read_traffic(workload)
+    result = {
+        "value": tflops, "ms_per_step": ms, "ms_per_step_eager": ms_eager,
+        "pct_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "config": {"workload": inp.name, "batch": B, "heads": H, "n_q": n_q, "n_kv": n_kv,
+                   "d_k": d_k, "d_v": d_v, "causal": inp.causal,
+                   "key_lengths": None if inp.seqlens_kv is None else "per-sequence",
+                   "cache": f"{'hot' if args.hot else 'cold'}: {R} rotating input sets of {per_set / 1e6:.1f} MB",
+                   "timing": "HIP graph of the timed steps, HIP events on the launch stream",
+                   "flops_per_step": flops, "algorithmic_bytes_per_step": algo_bytes},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "sdpa_fwd_bf16_d64", "algorithmic_bytes_per_launch": algo_bytes},
+    }
+    return result, inp, flops
+
+
+def bench_block(K, W, args):
+    import ctypes
+    import torch
+    import attn_inputs as gen
+    import head_attention_sdpa_amd as attn
+
+    L = attn.lib()
+    dev = torch.device("cuda:0")
+    inp = gen.config(5)
+    B, n, dm = inp.x.shape
+    h = inp.heads
+    hd = h * 64
+    x = to_dev(inp.x_st, "bf16", dev)
+    ws = [to_dev(w, "bf16", dev) for w in inp.w_st]
+    nbytes = attn.mha_workspace_bytes(B, n, n, dm, h)
+    work = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    y = torch.empty((B, n, dm), dtype=torch.bfloat16, device=dev)
+
+    def launch(s):
+        rc = L.attn_mha_fwd(attn.ATTN_BF16, B, n, n, dm, h, 64, 64, x.data_ptr(), x.data_ptr(),
+                            ws[0].data_ptr(), ws[1].data_ptr(), ws[2].data_ptr(), ws[3].data_ptr(),
+                            y.data_ptr(), float(inp.scale), attn.ATTN_MASK_CAUSAL, None, None,
+                            work.data_ptr(), nbytes, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"attn_mha_fwd failed: {attn.status_str(rc)}")
+
+    ms, _ = time_graph(launch, K, W, torch)
+
+    # the dominant kernel, SDPA, timed alone on the projection layout
+    qkv = work[: B * n * 3 * hd * 2].view(torch.bfloat16)
+    ocat = torch.empty((B, n, h, 64), dtype=torch.bfloat16, device=dev)
+    sq = attn.attn_strides(n * 3 * hd, 64, 3 * hd)
+    so = attn.attn_strides(n * hd, 64, hd)
+
+    def launch_sdpa(s):
+        rc = L.attn_sdpa_fwd(attn.ATTN_BF16, B, h, n, n, 64, 64, qkv.data_ptr(), ctypes.byref(sq),
+                             qkv.data_ptr() + hd * 2, ctypes.byref(sq), qkv.data_ptr() + 2 * hd * 2,
+                             ctypes.byref(sq), ocat.data_ptr(), ctypes.byref(so), float(inp.scale),
+                             attn.ATTN_MASK_CAUSAL, None, None, None,
+                             torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"attn_sdpa_fwd failed: {attn.status_str(rc)}")
+
+    ms_sdpa, _ = time_graph(launch_sdpa, max(10, K), W, torch)
+    pairs = legal_pairs(n, n, True, batch=1) * B * h
+    f_sdpa = pairs * 256
+    f_qkv = 2 * B * n * 3 * hd * dm
+    f_o = 2 * B * n * hd * dm
+    flops = f_sdpa + f_qkv + f_o
+    tflops = flops / (ms * 1e-3) / 1e12
+    sdpa_tflops = f_sdpa / (ms_sdpa * 1e-3) / 1e12
+    result = {
+        "value": tflops, "ms_per_step": ms, "pct_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "config": {"workload": inp.name, "batch": B, "n": n, "d_model": dm, "heads": h, "d_k": 64,
+                   "causal": True, "cache": "hot (inputs 48 MB, written intermediates reused)",
+                   "timing": "HIP graph of the timed steps, HIP events on the launch stream",
+                   "flops_per_step": flops,
+                   "sdpa_ms": ms_sdpa, "sdpa_tflops": sdpa_tflops},
+        "roofline": {"bound": "mfma", "achieved": sdpa_tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": sdpa_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": read_traffic("block"), "kernel": "sdpa_fwd_bf16_d64",
+                     "algorithmic_flops_per_launch": f_sdpa},
+    }
+    return result, inp, flops
+
+
+def cpu_baseline(cfg_id, inp, flops_full):
+    """The oracle as it stands, on the host cores, on a bounded sample."""
+    import oracle
+    threads = oracle.default_threads()
+    if cfg_id == 5:
+        # sample: batch element 0 of the block (a quarter of the workload)
+        x = inp.x[:1]
+        t0 = time.perf_counter()
+        oracle.mha(x, x, inp.w_q, inp.w_k, inp.w_v, inp.w_o, heads=inp.heads, causal=True,
+                   nthreads=threads)
+        dt = time.perf_counter() - t0
+        sample_flops = flops_full / inp.x.shape[0]
+        sample = "batch element 0 of 4 (all 4096 rows, projections + attention + W^O), one run"
+    else:
+        best = float("inf")
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.sdpa(inp.q, inp.k, inp.v, scale=inp.scale, causal=inp.causal,
+                        seqlens_q=inp.seqlens_q, seqlens_kv=inp.seqlens_kv, nthreads=threads)
+            best = min(best, time.perf_counter() - t0)
+        dt, sample_flops = best, flops_full
+        sample = "the full workload (every query row), best of 3"
+    return {"value": sample_flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decoder", choices=sorted(WORKLOAD_CFG))
+    ap.add_argument("--hot", action="store_true", help="reuse one input set (cache-hot)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cfg_id = WORKLOAD_CFG[args.workload]
+    K, W = args.steps, args.warmup
+    if cfg_id == 5:
+        res, inp, flops = bench_block(K, W, args)
+    else:
+        res, inp, flops = bench_sdpa(cfg_id, K, W, args)
+    out = {"metric": METRIC, "value": res["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+           "warmup": W, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": res["config"], "pct_mfma_peak": res["pct_mfma_peak"],
+           "roofline": res["roofline"]}
+    if "ms_per_step_eager" in res:
+        out["ms_per_step_eager"] = res["ms_per_step_eager"]
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg_id, inp, flops)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,185 @@
+"""MI355X (gfx950) scaled dot-product and multi-head attention.
+
+A thin ctypes binding over the C ABI in include/attn_sdpa.h (libattn_sdpa.so
+in this package directory).  This module only marshals arguments: every step
+of the computation runs in the library's HIP kernels.  PyTorch supplies the
+device memory and the current stream.  If the library is missing the calls
+raise; there is no fallback path.
+
+    sdpa(q, k, v, scale=None, causal=False, seqlens_q=None, seqlens_kv=None,
+         return_lse=False, out=None)
+        q [B,H,n_q,d_k], k [B,H,n_kv,d_k], v [B,H,n_kv,d_v] on the GPU, bf16 or
+        float32, last dimension contiguous.  Scaled dot-product attention,
+        "Attention Is All You Need" section 3.2.1 Eq. 1.
+
+    mha(x_q, x_kv, w_q, w_k, w_v, w_o, heads, ...)
+        Multi-head attention block, section 3.2.2 (no bias, Y = X.W).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_sdpa.so")
+
+ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_MASK_NONE, ATTN_MASK_CAUSAL = 0, 1
+STATUS = {0: "ATTN_OK", -1: "ATTN_E_INVALID", -2: "ATTN_E_UNSUPPORTED", -3: "ATTN_E_ALIGN",
+          -4: "ATTN_E_WORKSPACE", -5: "ATTN_E_HIP"}
+
+# every entry point that include/attn_sdpa.h declares
+EXPORTS = ("attn_sdpa_fwd", "attn_mha_workspace_bytes", "attn_mha_fwd", "attn_status_str",
+           "attn_abi_version")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+class attn_strides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("n", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C-ABI library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m head_attention_sdpa_amd.build` (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        i, vp, sp = ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(attn_strides)
+        L.attn_sdpa_fwd.argtypes = [i, i, i, i, i, i, i, vp, sp, vp, sp, vp, sp, vp, sp,
+                                    ctypes.c_float, i, vp, vp, vp, vp]
+        L.attn_sdpa_fwd.restype = i
+        L.attn_mha_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
+        L.attn_mha_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_mha_fwd.argtypes = [i, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp,
+                                   ctypes.c_float, i, vp, vp, vp, ctypes.c_size_t, vp]
+        L.attn_mha_fwd.restype = i
+        L.attn_status_str.argtypes = [i]
+        L.attn_status_str.restype = ctypes.c_char_p
+        L.attn_abi_version.argtypes = []
+        L.attn_abi_version.restype = i
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().attn_status_str(status).decode()
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise AttnError(fn, rc, status_str(rc))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _strides4(t) -> attn_strides:
+    if t.dim() == 4 and t.numel() == 0:  # empty: torch may report any strides
+        _, H, n, d = t.shape
+        return attn_strides(H * n * d, n * d, d)
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a [B,H,n,d] tensor with a contiguous last dimension")
+    return attn_strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _lens_ptr(lens, batch, device):
+    if lens is None:
+        return None
+    torch = _torch()
+    if not (isinstance(lens, torch.Tensor) and lens.dtype == torch.int32 and lens.device == device
+            and lens.is_contiguous() and lens.shape == (batch,)):
+        raise ValueError("lengths must be a contiguous int32 [batch] tensor on the same device")
+    return lens.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def sdpa(q, k, v, scale=None, causal=False, seqlens_q=None, seqlens_kv=None, return_lse=False,
+         out=None, stream=None):
+    """Scaled dot-product attention forward on the GPU (see module docstring).
+    Returns o [B,H,n_q,d_v] (and lse [B,H,n_q] fp32 if return_lse)."""
+    torch = _torch()
+    B, H, n_q, d_k = q.shape
+    n_kv, d_v = k.shape[2], v.shape[3]
+    if k.shape != (B, H, n_kv, d_k) or v.shape != (B, H, n_kv, d_v):
+        raise ValueError("shape mismatch between q, k, v")
+    if not (q.dtype == k.dtype == v.dtype) or not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must share dtype and device")
+    if q.device.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, H, n_q, d_v), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device) if return_lse else None
+    sq, sk, sv, so = _strides4(q), _strides4(k), _strides4(v), _strides4(out)
+    rc = lib().attn_sdpa_fwd(dt, B, H, n_q, n_kv, d_k, d_v,
+                             q.data_ptr(), ctypes.byref(sq), k.data_ptr(), ctypes.byref(sk),
+                             v.data_ptr(), ctypes.byref(sv), out.data_ptr(), ctypes.byref(so),
+                             0.0 if scale is None else float(scale),
+                             ATTN_MASK_CAUSAL if causal else ATTN_MASK_NONE,
+                             _lens_ptr(seqlens_q, B, q.device), _lens_ptr(seqlens_kv, B, q.device),
+                             None if lse is None else lse.data_ptr(), _stream(stream))
+    _check("attn_sdpa_fwd", rc)
+    return (out, lse) if return_lse else out
+
+
+def mha_workspace_bytes(batch, n_q, n_kv, d_model, heads, d_k=64, d_v=64, dtype=ATTN_BF16) -> int:
+    return int(lib().attn_mha_workspace_bytes(dtype, batch, n_q, n_kv, d_model, heads, d_k, d_v))
+
+
+def mha(x_q, x_kv, w_q, w_k, w_v, w_o, heads, scale=None, causal=False, seqlens_q=None,
+        seqlens_kv=None, out=None, workspace=None, stream=None):
+    """Multi-head attention block forward on the GPU (bf16, d_k = d_v = 64).
+    x_q [B,n_q,d_model], x_kv [B,n_kv,d_model] (pass x_q itself for
+    self-attention); w_q/w_k/w_v [d_model, heads*64], w_o [heads*64, d_model].
+    Returns y [B,n_q,d_model]."""
+    torch = _torch()
+    B, n_q, d_model = x_q.shape
+    n_kv = x_kv.shape[1]
+    d_k = w_q.shape[1] // heads
+    d_v = w_v.shape[1] // heads
+    for t in (x_q, x_kv, w_q, w_k, w_v, w_o):
+        if not t.is_contiguous() or t.device != x_q.device or t.dtype != x_q.dtype:
+            raise ValueError("mha inputs must be contiguous and share device and dtype")
+    dt = _dtype_code(x_q)
+    nbytes = mha_workspace_bytes(B, n_q, n_kv, d_model, heads, d_k, d_v, dt)
+    if nbytes == 0:
+        raise AttnError("attn_mha_workspace_bytes", -2, "unsupported sizes")
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x_q.device)
+    if out is None:
+        out = torch.empty((B, n_q, d_model), dtype=x_q.dtype, device=x_q.device)
+    rc = lib().attn_mha_fwd(dt, B, n_q, n_kv, d_model, heads, d_k, d_v,
+                            x_q.data_ptr(), x_kv.data_ptr(), w_q.data_ptr(), w_k.data_ptr(),
+                            w_v.data_ptr(), w_o.data_ptr(), out.data_ptr(),
+                            0.0 if scale is None else float(scale),
+                            ATTN_MASK_CAUSAL if causal else ATTN_MASK_NONE,
+                            _lens_ptr(seqlens_q, B, x_q.device), _lens_ptr(seqlens_kv, B, x_q.device),
+                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                            _stream(stream))
+    _check("attn_mha_fwd", rc)
+    return out

@@ -1,0 +1,276 @@
+// C ABI of the attention library: host-side validation, layout bookkeeping
+// and launches.  Every argument is checked before anything is enqueued, so an
+// error never leaves a partial launch behind.  No allocation, no
+// synchronisation, no printing.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/attn_sdpa.h"
+#include "internal.h"
+
+namespace {
+
+using attn::GemmBf16Params;
+using attn::SdpaBf16Params;
+using attn::SdpaF32Params;
+
+constexpr int kMaxGrid = 0x7fffffff;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Contiguous [batch, heads, n, d] strides when s is null.
+attn_strides resolve(const attn_strides* s, int heads, int n, int d) {
+  if (s) return *s;
+  attn_strides c;
+  c.n = d;
+  c.h = (int64_t)n * d;
+  c.b = (int64_t)heads * n * d;
+  return c;
+}
+
+bool strides_ok(const attn_strides& s) { return s.b >= 0 && s.h >= 0 && s.n >= 0; }
+
+bool strides_aligned(const attn_strides& s, int64_t elems) {
+  return s.b % elems == 0 && s.h % elems == 0 && s.n % elems == 0;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_HIP; }
+
+// Shared checks of the SDPA arguments; fills the resolved strides and scale.
+int check_sdpa(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k, int d_v,
+               const void* q, const attn_strides* sq, const void* k, const attn_strides* sk,
+               const void* v, const attn_strides* sv, void* o, const attn_strides* so,
+               float* scale, attn_mask mask, const float* lse, attn_strides out[4]) {
+  if (dt != ATTN_F32 && dt != ATTN_BF16) return ATTN_E_INVALID;
+  if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL) return ATTN_E_INVALID;
+  if (batch < 1 || heads < 1 || n_q < 0 || n_kv < 0 || d_k < 1 || d_v < 1) return ATTN_E_INVALID;
+  if (!q || !k || !v || !o) return ATTN_E_INVALID;
+  if (*scale == 0.f) *scale = 1.f / sqrtf((float)d_k);
+  if (!(isfinite(*scale) && *scale > 0.f)) return ATTN_E_INVALID;
+  out[0] = resolve(sq, heads, n_q, d_k);
+  out[1] = resolve(sk, heads, n_kv, d_k);
+  out[2] = resolve(sv, heads, n_kv, d_v);
+  out[3] = resolve(so, heads, n_q, d_v);
+  for (int t = 0; t < 4; ++t)
+    if (!strides_ok(out[t])) return ATTN_E_INVALID;
+  if (dt == ATTN_BF16) {
+    if (d_k != 64 || d_v != 64) return ATTN_E_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return ATTN_E_ALIGN;
+    for (int t = 0; t < 4; ++t)
+      if (!strides_aligned(out[t], 8)) return ATTN_E_ALIGN;
+    const int64_t qblocks = (n_q + 127) / 128;
+    if (qblocks * batch * heads > kMaxGrid) return ATTN_E_UNSUPPORTED;
+  } else {
+    if (d_k > 64 || d_v > 64) return ATTN_E_UNSUPPORTED;
+    if (!aligned(q, 4) || !aligned(k, 4) || !aligned(v, 4) || !aligned(o, 4)) return ATTN_E_ALIGN;
+    if (heads > 65535 || batch > 65535) return ATTN_E_UNSUPPORTED;
+  }
+  if (lse && !aligned(lse, 4)) return ATTN_E_ALIGN;
+  return ATTN_OK;
+}
+
+int launch_sdpa(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k, int d_v,
+                const void* q, const void* k, const void* v, void* o, const attn_strides st[4],
+                float scale, attn_mask mask, const int32_t* lq, const int32_t* lkv, float* lse,
+                hipStream_t stream) {
+  if (dt == ATTN_BF16) {
+    SdpaBf16Params p = {};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.o = static_cast<uint16_t*>(o);
+    p.lse = lse;
+    p.seqlens_q = lq;
+    p.seqlens_kv = lkv;
+    p.qs_b = st[0].b; p.qs_h = st[0].h; p.qs_n = st[0].n;
+    p.ks_b = st[1].b; p.ks_h = st[1].h; p.ks_n = st[1].n;
+    p.vs_b = st[2].b; p.vs_h = st[2].h; p.vs_n = st[2].n;
+    p.os_b = st[3].b; p.os_h = st[3].h; p.os_n = st[3].n;
+    p.batch = batch; p.heads = heads; p.n_q = n_q; p.n_kv = n_kv;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.causal = mask == ATTN_MASK_CAUSAL;
+    return hip_status(attn::launch_sdpa_bf16(p, stream));
+  }
+  SdpaF32Params p = {};
+  p.q = static_cast<const float*>(q);
+  p.k = static_cast<const float*>(k);
+  p.v = static_cast<const float*>(v);
+  p.o = static_cast<float*>(o);
+  p.lse = lse;
+  p.seqlens_q = lq;
+  p.seqlens_kv = lkv;
+  p.qs_b = st[0].b; p.qs_h = st[0].h; p.qs_n = st[0].n;
+  p.ks_b = st[1].b; p.ks_h = st[1].h; p.ks_n = st[1].n;
+  p.vs_b = st[2].b; p.vs_h = st[2].h; p.vs_n = st[2].n;
+  p.os_b = st[3].b; p.os_h = st[3].h; p.os_n = st[3].n;
+  p.batch = batch; p.heads = heads; p.n_q = n_q; p.n_kv = n_kv; p.d_k = d_k; p.d_v = d_v;
+  p.scale = scale;
+  p.causal = mask == ATTN_MASK_CAUSAL;
+  return hip_status(attn::launch_sdpa_f32(p, stream));
+}
+
+// Workspace regions of the MHA block (bf16 elements), each 256-byte aligned.
+struct MhaLayout {
+  size_t q_off, kv_off, o_off, total_bytes;  // byte offsets
+};
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool mha_sizes_ok(attn_dtype dt, int batch, int n_q, int n_kv, int d_model, int heads, int d_k,
+                  int d_v, int* err) {
+  if (dt != ATTN_F32 && dt != ATTN_BF16) { *err = ATTN_E_INVALID; return false; }
+  if (batch < 1 || n_q < 0 || n_kv < 0 || d_model < 1 || heads < 1 || d_k < 1 || d_v < 1) {
+    *err = ATTN_E_INVALID;
+    return false;
+  }
+  if (dt != ATTN_BF16 || d_k != 64 || d_v != 64 || d_model % 64 != 0) {
+    *err = ATTN_E_UNSUPPORTED;
+    return false;
+  }
+  // GEMM row counts and workspace offsets must fit the kernels' index types
+  if ((int64_t)batch * n_q > kMaxGrid || (int64_t)batch * n_kv > kMaxGrid ||
+      (int64_t)heads * 64 * 3 > kMaxGrid) {
+    *err = ATTN_E_UNSUPPORTED;
+    return false;
+  }
+  return true;
+}
+
+MhaLayout mha_layout(int batch, int n_q, int n_kv, int heads) {
+  const size_t hd = (size_t)heads * 64;
+  MhaLayout L;
+  L.q_off = 0;                                                   // Q  [B*n_q, H*64]
+  L.kv_off = round256(L.q_off + (size_t)batch * n_q * hd * 2);   // KV [B*n_kv, 2*H*64]
+  L.o_off = round256(L.kv_off + (size_t)batch * n_kv * 2 * hd * 2);  // Ocat [B*n_q, H*64]
+  L.total_bytes = round256(L.o_off + (size_t)batch * n_q * hd * 2);
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char* attn_status_str(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_E_INVALID: return "invalid argument";
+    case ATTN_E_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_E_ALIGN: return "misaligned pointer or stride";
+    case ATTN_E_WORKSPACE: return "workspace missing or too small";
+    case ATTN_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int attn_sdpa_fwd(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k, int d_v,
+                  const void* q, const attn_strides* sq, const void* k, const attn_strides* sk,
+                  const void* v, const attn_strides* sv, void* o, const attn_strides* so,
+                  float scale, attn_mask mask, const int32_t* seqlens_q,
+                  const int32_t* seqlens_kv, float* lse, attn_stream_t stream) {
+  attn_strides st[4];
+  const int rc = check_sdpa(dt, batch, heads, n_q, n_kv, d_k, d_v, q, sq, k, sk, v, sv, o, so,
+                            &scale, mask, lse, st);
+  if (rc != ATTN_OK) return rc;
+  return launch_sdpa(dt, batch, heads, n_q, n_kv, d_k, d_v, q, k, v, o, st, scale, mask,
+                     seqlens_q, seqlens_kv, lse, static_cast<hipStream_t>(stream));
+}
+
+size_t attn_mha_workspace_bytes(attn_dtype dt, int batch, int n_q, int n_kv, int d_model,
+                                int heads, int d_k, int d_v) {
+  int err;
+  if (!mha_sizes_ok(dt, batch, n_q, n_kv, d_model, heads, d_k, d_v, &err)) return 0;
+  return mha_layout(batch, n_q, n_kv, heads).total_bytes;
+}
+
+int attn_mha_fwd(attn_dtype dt, int batch, int n_q, int n_kv, int d_model, int heads, int d_k,
+                 int d_v, const void* x_q, const void* x_kv, const void* w_q, const void* w_k,
+                 const void* w_v, const void* w_o, void* y, float scale, attn_mask mask,
+                 const int32_t* seqlens_q, const int32_t* seqlens_kv, void* workspace,
+                 size_t workspace_bytes, attn_stream_t stream_) {
+  int err = ATTN_OK;
+  if (!mha_sizes_ok(dt, batch, n_q, n_kv, d_model, heads, d_k, d_v, &err)) return err;
+  if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL) return ATTN_E_INVALID;
+  if (!x_q || !x_kv || !w_q || !w_k || !w_v || !w_o || !y) return ATTN_E_INVALID;
+  if (scale == 0.f) scale = 1.f / sqrtf((float)d_k);
+  if (!(isfinite(scale) && scale > 0.f)) return ATTN_E_INVALID;
+  const void* ptrs[] = {x_q, x_kv, w_q, w_k, w_v, w_o, y};
+  for (const void* p : ptrs)
+    if (!aligned(p, 16)) return ATTN_E_ALIGN;
+  const MhaLayout L = mha_layout(batch, n_q, n_kv, heads);
+  if (!workspace || workspace_bytes < L.total_bytes) return ATTN_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return ATTN_E_ALIGN;
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* qbuf = reinterpret_cast<uint16_t*>(ws + L.q_off);
+  uint16_t* kvbuf = reinterpret_cast<uint16_t*>(ws + L.kv_off);
+  uint16_t* obuf = reinterpret_cast<uint16_t*>(ws + L.o_off);
+  const int hd = heads * 64;
+
+  attn_strides st[4];
+  const uint16_t *qp, *kp, *vp;
+  int rc;
+  if (x_kv == x_q && n_kv == n_q) {
+    // 1. self-attention: one GEMM over the three weight panels,
+    //    [Q | K | V] = X [W^Q | W^K | W^V] -> [B*n, 3*H*64] at the start of the
+    //    workspace (it fits before the concatenation region)
+    GemmBf16Params g = {};
+    g.a = static_cast<const uint16_t*>(x_q);
+    g.b[0] = static_cast<const uint16_t*>(w_q);
+    g.b[1] = static_cast<const uint16_t*>(w_k);
+    g.b[2] = static_cast<const uint16_t*>(w_v);
+    g.c = qbuf;
+    g.lda = d_model; g.ldc = 3 * hd; g.M = batch * n_q; g.N = 3 * hd; g.K = d_model; g.n_panel = hd;
+    rc = hip_status(attn::launch_gemm_bf16(g, stream));
+    st[0] = attn_strides{(int64_t)n_q * 3 * hd, 64, 3 * hd};
+    st[1] = st[2] = st[0];
+    qp = qbuf;
+    kp = qbuf + hd;
+    vp = qbuf + 2 * hd;
+  } else {
+    // 1. cross-attention: Q = X_q W^Q -> [B*n_q, H*64];
+    //    [K | V] = X_kv [W^K | W^V] -> [B*n_kv, 2*H*64]
+    GemmBf16Params gq = {};
+    gq.a = static_cast<const uint16_t*>(x_q);
+    gq.b[0] = static_cast<const uint16_t*>(w_q);
+    gq.c = qbuf;
+    gq.lda = d_model; gq.ldc = hd; gq.M = batch * n_q; gq.N = hd; gq.K = d_model; gq.n_panel = hd;
+    GemmBf16Params gkv = {};
+    gkv.a = static_cast<const uint16_t*>(x_kv);
+    gkv.b[0] = static_cast<const uint16_t*>(w_k);
+    gkv.b[1] = static_cast<const uint16_t*>(w_v);
+    gkv.c = kvbuf;
+    gkv.lda = d_model; gkv.ldc = 2 * hd; gkv.M = batch * n_kv; gkv.N = 2 * hd; gkv.K = d_model;
+    gkv.n_panel = hd;
+    rc = hip_status(attn::launch_gemm_bf16(gq, stream));
+    if (rc == ATTN_OK) rc = hip_status(attn::launch_gemm_bf16(gkv, stream));
+    st[0] = attn_strides{(int64_t)n_q * hd, 64, hd};
+    st[1] = attn_strides{(int64_t)n_kv * 2 * hd, 64, 2 * hd};
+    st[2] = st[1];
+    qp = qbuf;
+    kp = kvbuf;
+    vp = kvbuf + hd;
+  }
+  if (rc != ATTN_OK) return rc;
+
+  // 2. attention per head, reading the projections through strides and
+  //    writing the concatenation [B, n_q, H, 64] directly
+  st[3] = attn_strides{(int64_t)n_q * hd, 64, hd};
+  rc = launch_sdpa(ATTN_BF16, batch, heads, n_q, n_kv, 64, 64, qp, kp, vp, obuf, st, scale, mask,
+                   seqlens_q, seqlens_kv, nullptr, stream);
+  if (rc != ATTN_OK) return rc;
+
+  // 3. output projection: Y = Ocat W^O -> [B*n_q, d_model]
+  GemmBf16Params go = {};
+  go.a = obuf;
+  go.b[0] = static_cast<const uint16_t*>(w_o);
+  go.c = static_cast<uint16_t*>(y);
+  go.lda = hd; go.ldc = d_model; go.M = batch * n_q; go.N = d_model; go.K = hd; go.n_panel = d_model;
+  return hip_status(attn::launch_gemm_bf16(go, stream));
+}
+
+}  // extern "C"

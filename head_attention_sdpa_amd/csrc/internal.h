@@ -1,0 +1,67 @@
+// Internal declarations shared by the library's HIP sources (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Scaled dot-product attention, bf16 storage, head size 64.
+struct SdpaBf16Params {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;                   // [batch*heads*n_q] or null
+  const int32_t* seqlens_q;     // [batch] or null
+  const int32_t* seqlens_kv;    // [batch] or null
+  int64_t qs_b, qs_h, qs_n;     // element strides (d stride 1)
+  int64_t ks_b, ks_h, ks_n;
+  int64_t vs_b, vs_h, vs_n;
+  int64_t os_b, os_h, os_n;
+  int batch, heads, n_q, n_kv;
+  int n_qblocks;                // ceil(n_q / queries per workgroup)
+  float scale_log2;             // scale * log2(e): scores go straight to exp2
+  int causal;
+};
+
+// Scaled dot-product attention, fp32 storage and arithmetic, head sizes <= 64.
+struct SdpaF32Params {
+  const float* q;
+  const float* k;
+  const float* v;
+  float* o;
+  float* lse;
+  const int32_t* seqlens_q;
+  const int32_t* seqlens_kv;
+  int64_t qs_b, qs_h, qs_n;
+  int64_t ks_b, ks_h, ks_n;
+  int64_t vs_b, vs_h, vs_n;
+  int64_t os_b, os_h, os_n;
+  int batch, heads, n_q, n_kv, d_k, d_v;
+  float scale;
+  int causal;
+};
+
+// C[M, N] = A[M, K] . B[K, N], bf16 in, fp32 accumulate, bf16 out (RNE).
+// A row-major with row stride lda; B given as up to three row-major column
+// panels (B = [B0 | B1 | B2], each [K, n_panel]); C row-major with stride ldc.
+struct GemmBf16Params {
+  const uint16_t* a;
+  const uint16_t* b[3];
+  uint16_t* c;
+  int64_t lda, ldc;
+  int M, N, K;
+  int n_panel;                  // columns per B panel (N = panels * n_panel)
+};
+
+// Launchers: return hipSuccess or the launch error.  Shapes are validated by
+// the caller (abi.cpp) before these are reached.
+hipError_t launch_sdpa_bf16(const SdpaBf16Params& p, hipStream_t stream);
+hipError_t launch_sdpa_f32(const SdpaF32Params& p, hipStream_t stream);
+hipError_t launch_gemm_bf16(const GemmBf16Params& p, hipStream_t stream);
+
+// Queries per workgroup of the bf16 SDPA kernel chosen for these sizes.
+int sdpa_bf16_block_m(int batch, int heads, int n_q);
+
+}  // namespace attn

@@ -1,0 +1,144 @@
+/*
+ * attn_sdpa.h -- C ABI of the MI355X (gfx950) attention library.
+ *
+ * Operations (definitions as in "Attention Is All You Need"):
+ *   attn_sdpa_fwd  scaled dot-product attention, section 3.2.1, Eq. 1:
+ *                  O = softmax(Q K^T * scale) V per (batch, head), scale
+ *                  defaulting to 1/sqrt(d_k) (footnote 4 of the paper; the
+ *                  variance argument is restated in the rockcohen.cc deep read,
+ *                  section 5.1).
+ *   attn_mha_fwd   multi-head attention, section 3.2.2:
+ *                  Y = Concat(head_1..head_h) W^O,
+ *                  head_i = Attention(X_q W_i^Q, X_kv W_i^K, X_kv W_i^V)
+ *                  (restated on the vlmlib.cn summary and rockcohen.cc 5.2).
+ *                  Self-attention passes x_kv == x_q; encoder-decoder
+ *                  attention passes the encoder output as x_kv (section 3.2.3;
+ *                  rockcohen.cc 5.3).
+ *
+ * Masking.  Key j is legal for query i iff j < L_kv[b] (when key lengths are
+ * given) and, with ATTN_MASK_CAUSAL, j <= i (the decoder's illegal
+ * connections, set to -inf before the softmax: rockcohen.cc 5.3 and 6.3;
+ * the diagonal stays legal).  Causal masking is aligned at the top-left
+ * (query i, key i) for any n_q, n_kv.  Illegal keys get weight exactly 0 and
+ * their K/V memory is never used in the arithmetic (it may hold NaN).  A query
+ * row with no legal key, and every row i >= L_q[b] when query lengths are
+ * given, is written as zeros (and its lse as -inf).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or synchronises; it only enqueues
+ *     kernels on `stream` (a hipStream_t; NULL = the null stream) and returns.
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error nothing is enqueued and a negative attn_status is returned.
+ *     Nothing is printed.  Asynchronous device faults surface at the caller's
+ *     next synchronisation.
+ *   - Lengths arrays are device int32 [batch]; values are clamped to [0, n].
+ *   - Thread safety: calls may be made from several host threads; the library
+ *     keeps only a lazily initialised per-device properties cache.
+ */
+#ifndef ATTN_SDPA_H
+#define ATTN_SDPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef void* attn_stream_t; /* hipStream_t */
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+typedef enum { ATTN_MASK_NONE = 0, ATTN_MASK_CAUSAL = 1 } attn_mask;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_E_INVALID = -1,     /* null pointer, negative size, bad enum, scale not finite/positive */
+  ATTN_E_UNSUPPORTED = -2, /* valid but not implemented (head size, dtype, ...) */
+  ATTN_E_ALIGN = -3,       /* pointer or stride misaligned for the vector loads */
+  ATTN_E_WORKSPACE = -4,   /* workspace missing or too small */
+  ATTN_E_HIP = -5          /* the HIP runtime rejected a launch */
+} attn_status;
+
+/* Element strides of a [batch, heads, n, d] tensor; the d stride is always 1.
+ * Passing NULL for a strides pointer means contiguous [batch, heads, n, d]. */
+typedef struct {
+  int64_t b, h, n;
+} attn_strides;
+
+/*
+ * attn_sdpa_fwd -- scaled dot-product attention, forward.
+ *
+ *   q  [batch, heads, n_q,  d_k]   o   [batch, heads, n_q, d_v]
+ *   k  [batch, heads, n_kv, d_k]   lse [batch, heads, n_q] fp32, contiguous
+ *   v  [batch, heads, n_kv, d_v]       (natural log of the softmax denominator,
+ *                                       lse = max_j s_j + ln sum_j e^{s_j - max})
+ *   dt          ATTN_BF16: q/k/v/o are bf16; products accumulate in fp32, the
+ *               weights are rounded to bf16 for the P.V product, and O is
+ *               rounded to bf16 once (round to nearest even).
+ *               ATTN_F32: q/k/v/o are fp32, all arithmetic fp32.
+ *   batch, heads >= 1; n_q, n_kv >= 0
+ *   d_k, d_v    bf16: d_k = d_v = 64.  f32: 1 <= d_k, d_v <= 64.
+ *   sq, sk, sv, so  element strides (NULL = contiguous); bf16 needs every
+ *               stride and base pointer 16-byte aligned; f32 needs 4 bytes.
+ *   scale       0 means 1/sqrt(d_k); otherwise must be finite and > 0.
+ *   mask        ATTN_MASK_NONE or ATTN_MASK_CAUSAL.
+ *   seqlens_q   device int32 [batch] or NULL.
+ *   seqlens_kv  device int32 [batch] or NULL.
+ *   lse         device fp32 [batch*heads*n_q] or NULL.
+ * Returns ATTN_OK or a negative attn_status.  o must not alias q, k or v.
+ */
+int attn_sdpa_fwd(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k, int d_v,
+                  const void* q, const attn_strides* sq, const void* k, const attn_strides* sk,
+                  const void* v, const attn_strides* sv, void* o, const attn_strides* so,
+                  float scale, attn_mask mask, const int32_t* seqlens_q,
+                  const int32_t* seqlens_kv, float* lse, attn_stream_t stream);
+
+/*
+ * attn_mha_workspace_bytes -- workspace that attn_mha_fwd needs for these
+ * sizes (projections and the head concatenation, bf16), or 0 if the sizes
+ * are invalid or unsupported.
+ */
+size_t attn_mha_workspace_bytes(attn_dtype dt, int batch, int n_q, int n_kv, int d_model,
+                                int heads, int d_k, int d_v);
+
+/*
+ * attn_mha_fwd -- multi-head attention block, forward (no bias, as in the
+ * formula of section 3.2.2).
+ *
+ *   x_q   [batch, n_q,  d_model] bf16 (queries; the decoder side)
+ *   x_kv  [batch, n_kv, d_model] bf16 (keys/values; may equal x_q)
+ *   w_q, w_k  [d_model, heads*d_k] row-major, Y = X.W (head h owns columns
+ *             [h*d_k, (h+1)*d_k))
+ *   w_v       [d_model, heads*d_v]
+ *   w_o       [heads*d_v, d_model]  (row h*d_v + c of the concatenation is
+ *             head h's output column c)
+ *   y         [batch, n_q, d_model] bf16, written in full
+ *   dt        ATTN_BF16 only; d_k = d_v = 64; d_model a multiple of 64.
+ *   scale, mask, seqlens_q, seqlens_kv: as in attn_sdpa_fwd (padded query
+ *             rows give zero rows of y).
+ *   workspace device memory of at least attn_mha_workspace_bytes(...) bytes,
+ *             256-byte aligned; contents on entry are ignored.
+ * All inputs must be contiguous and 16-byte aligned.  y must not alias any
+ * input or the workspace.
+ */
+int attn_mha_fwd(attn_dtype dt, int batch, int n_q, int n_kv, int d_model, int heads, int d_k,
+                 int d_v, const void* x_q, const void* x_kv, const void* w_q, const void* w_k,
+                 const void* w_v, const void* w_o, void* y, float scale, attn_mask mask,
+                 const int32_t* seqlens_q, const int32_t* seqlens_kv, void* workspace,
+                 size_t workspace_bytes, attn_stream_t stream);
+
+/* Human-readable name of an attn_status value (static storage). */
+const char* attn_status_str(int status);
+
+/* ATTN_ABI_VERSION of the loaded library. */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_SDPA_H */

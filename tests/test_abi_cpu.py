@@ -1,0 +1,108 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point the
+header declares, and rejects bad arguments with the documented status before
+touching the GPU.  Every call here fails validation by construction (fake
+device pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import head_attention_sdpa_amd as attn
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "attn_sdpa.h")
+FAKE = 0x10000          # 16-byte aligned, never dereferenced
+MISALIGNED = 0x10002
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_header_symbols():
+    L = attn.lib()
+    names = header_functions()
+    assert set(names) == set(attn.EXPORTS)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define ATTN_ABI_VERSION (\d+)", open(HEADER).read())
+    assert attn.lib().attn_abi_version() == int(m.group(1))
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert attn.status_str(code) and attn.status_str(code) != "unknown status"
+    assert attn.status_str(42) == "unknown status"
+
+
+def sdpa_call(dt=1, B=2, H=2, nq=8, nkv=8, dk=64, dv=64, q=FAKE, k=FAKE, v=FAKE, o=FAKE,
+              sq=None, scale=0.0, mask=0, lse=None):
+    sqp = ctypes.byref(sq) if sq is not None else None
+    return attn.lib().attn_sdpa_fwd(dt, B, H, nq, nkv, dk, dv, q, sqp, k, None, v, None, o, None,
+                                    scale, mask, None, None, lse, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), -1),
+    (dict(B=0), -1),
+    (dict(H=-1), -1),
+    (dict(nq=-1), -1),
+    (dict(dk=0), -1),
+    (dict(q=None), -1),
+    (dict(o=None), -1),
+    (dict(scale=-1.0), -1),
+    (dict(scale=float("inf")), -1),
+    (dict(scale=float("nan")), -1),
+    (dict(mask=3), -1),
+    (dict(sq=attn.attn_strides(-8, 64, 64)), -1),
+    (dict(dk=32), -2),
+    (dict(dv=128), -2),
+    (dict(dt=0, dk=65), -2),
+    (dict(q=MISALIGNED), -3),
+    (dict(o=MISALIGNED), -3),
+    (dict(sq=attn.attn_strides(1024, 512, 68)), -3),
+    (dict(dt=0, q=MISALIGNED), -3),
+    (dict(lse=MISALIGNED), -3),
+])
+def test_sdpa_validation(kw, code):
+    assert sdpa_call(**kw) == code
+
+
+def mha_call(dt=1, B=1, nq=16, nkv=16, dm=128, H=2, dk=64, dv=64, ws=FAKE, wsb=1 << 30,
+             x=FAKE, y=FAKE, scale=0.0, mask=1):
+    return attn.lib().attn_mha_fwd(dt, B, nq, nkv, dm, H, dk, dv, x, x, FAKE, FAKE, FAKE, FAKE, y,
+                                   scale, mask, None, None, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=5), -1),
+    (dict(B=0), -1),
+    (dict(x=None), -1),
+    (dict(scale=-2.0), -1),
+    (dict(mask=9), -1),
+    (dict(dt=0), -2),
+    (dict(dk=32), -2),
+    (dict(dm=100), -2),
+    (dict(ws=None), -4),
+    (dict(wsb=1024), -4),
+    (dict(ws=FAKE + 16), -3),
+    (dict(y=MISALIGNED), -3),
+])
+def test_mha_validation(kw, code):
+    assert mha_call(**kw) == code
+
+
+def test_mha_workspace_bytes():
+    L = attn.lib()
+    # cfg: 4 x 4096 tokens, d_model 1024, 16 heads: Q, K, V and the concatenation in bf16
+    n = L.attn_mha_workspace_bytes(1, 4, 4096, 4096, 1024, 16, 64, 64)
+    assert n == 4 * 4096 * 1024 * 2 * 4
+    assert L.attn_mha_workspace_bytes(0, 4, 4096, 4096, 1024, 16, 64, 64) == 0  # f32 unsupported
+    assert L.attn_mha_workspace_bytes(1, 4, 4096, 4096, 1000, 16, 64, 64) == 0
+    assert L.attn_mha_workspace_bytes(1, 0, 4096, 4096, 1024, 16, 64, 64) == 0
