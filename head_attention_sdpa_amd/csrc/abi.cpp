@@ -46,7 +46,8 @@ int check_sdpa(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k, 
   if (dt != ATTN_F32 && dt != ATTN_BF16) return ATTN_E_INVALID;
   if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL) return ATTN_E_INVALID;
   if (batch < 1 || heads < 1 || n_q < 0 || n_kv < 0 || d_k < 1 || d_v < 1) return ATTN_E_INVALID;
-  if (!q || !k || !v || !o) return ATTN_E_INVALID;
+  // a tensor with no rows may be a null pointer
+  if ((n_q > 0 && (!q || !o)) || (n_kv > 0 && (!k || !v))) return ATTN_E_INVALID;
   if (*scale == 0.f) *scale = 1.f / sqrtf((float)d_k);
   if (!(isfinite(*scale) && *scale > 0.f)) return ATTN_E_INVALID;
   out[0] = resolve(sq, heads, n_q, d_k);
@@ -62,6 +63,17 @@ int check_sdpa(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k, 
       if (!strides_aligned(out[t], 8)) return ATTN_E_ALIGN;
     const int64_t qblocks = (n_q + 127) / 128;
     if (qblocks * batch * heads > kMaxGrid) return ATTN_E_UNSUPPORTED;
+    // Q/K/V rows are fetched through 32-bit buffer offsets from each (b, h)
+    // slice, and rows past the lengths must fall outside the buffer range:
+    // rows may not overlap and a slice (rounded up to 64 rows) must stay
+    // below 2 GiB.
+    if (n_kv > 1 && (out[1].n < 64 || out[2].n < 64)) return ATTN_E_UNSUPPORTED;
+    if (n_q > 1 && out[0].n < 64) return ATTN_E_UNSUPPORTED;
+    const int64_t rows = ((int64_t)n_kv + 63) / 64 * 64;
+    const int64_t qrows = ((int64_t)n_q + 127) / 128 * 128;
+    if (rows * out[1].n * 2 + 128 > 0x7fffffffLL || rows * out[2].n * 2 + 128 > 0x7fffffffLL ||
+        qrows * out[0].n * 2 + 128 > 0x7fffffffLL)
+      return ATTN_E_UNSUPPORTED;
   } else {
     if (d_k > 64 || d_v > 64) return ATTN_E_UNSUPPORTED;
     if (!aligned(q, 4) || !aligned(k, 4) || !aligned(v, 4) || !aligned(o, 4)) return ATTN_E_ALIGN;

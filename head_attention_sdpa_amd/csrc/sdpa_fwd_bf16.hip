@@ -48,8 +48,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = 64;         // head size (d_k = d_v)
 constexpr int BN = 64;        // keys per iteration
-constexpr int LDS_ROW = 72;   // bf16 per LDS row: 64 + 8 pad (144 B) -> conflict-free row reads
-constexpr int TILE = BN * LDS_ROW;
 constexpr float LN2 = 0.69314718055994530942f;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -92,16 +90,66 @@ __device__ __forceinline__ void map_block(int bid, int bh_total, int nqb, int ca
   qb = causal ? nqb - 1 - qb_idx : qb_idx;
 }
 
-template <int NW>
+// LDS tile layout: 64 rows x 128 B, no padding; the 16-byte chunk c of row r
+// is stored at chunk position c ^ swz(r), so that the lane patterns of the
+// two readers hit distinct banks:
+//   K (rows of 16 consecutive keys, one chunk each):  swz = (r >> 1) & 7
+//   V (transposed reads of 4 rows x 2 or 4 chunks):    swz = ((r >> 1) & 1) << 2
+__device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz_v(int r) { return ((r >> 1) & 1) << 2; }
+
+// Global -> LDS copies (16 bytes per lane, lane i lands at M0 + 16*i) are
+// issued from inline assembly and waited for explicitly with vmcnt: the
+// compiler then never inserts its own conservative "all DMA done" waits in
+// front of LDS reads, which would drain the prefetch ring every iteration.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor: 48-bit base, stride 0, range in bytes; reads at or
+// past the range return zeros.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32) & 0xffff, (int)bytes, 0x00020000};
+}
+
+__device__ __forceinline__ void dma16(uint32_t voff, i32x4 rsrc, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               ::"v"(voff), "s"(rsrc), "s"(lds_addr) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// wait until at most n (a multiple of Step, n <= 4*Step) DMA instructions are in flight
+template <int Step>
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  if (n <= 0) wait_vmcnt<0>();
+  else if (n <= Step) wait_vmcnt<Step>();
+  else if (n <= 2 * Step) wait_vmcnt<2 * Step>();
+  else if (n <= 3 * Step) wait_vmcnt<3 * Step>();
+  else wait_vmcnt<4 * Step>();
+}
+// The wave's own LDS reads are complete, then all waves meet.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>(p);
+}
+
+template <int NW, int NS>
 __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_d64(const SdpaBf16Params p) {
-  constexpr int BM = 32 * NW;          // queries per workgroup
-  constexpr int NT = 64 * NW;          // threads per workgroup
-  constexpr int CPT = (BN * D / 8) / NT;  // 16-byte chunks per thread per tile
-  static_assert(CPT * NT == BN * D / 8, "tile must split evenly");
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * 2 * TILE];  // [buf][K, V][64][72]
+  constexpr int BM = 32 * NW;            // queries per workgroup
+  constexpr int TILE_E = BN * D;         // bf16 elements per K or V tile (8 KiB)
+  constexpr int IPT = 16 / NW;           // DMA instructions per wave per stage (8 K + 8 V row blocks)
+  static_assert(IPT * NW == 16 && NS >= 2, "bad configuration");
+  static_assert(NW * 32 * D <= 2 * TILE_E, "the Q rows must fit in one ring stage");
+  __shared__ __attribute__((aligned(1024))) __bf16 smem[NS * 2 * TILE_E];  // [stage][K, V][64][64]
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: DMA targets live in SGPRs
   const int i32 = lane & 31, g = lane >> 5;
 
   int bh, qb;
@@ -116,11 +164,11 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_d64(const SdpaBf16Param
   const int qw0 = q0 + wave * 32;
   const int qi = qw0 + i32;
 
-  // keys this workgroup / this wave needs
+  // keys this workgroup / this wave needs (queries >= Lq are zeros: need nothing)
   int kv_end = Lkv, wkv_end = Lkv;
   if (p.causal) {
-    kv_end = min(kv_end, q0 + BM);
-    wkv_end = min(wkv_end, qw0 + 32);
+    kv_end = min(kv_end, min(q0 + BM, Lq));
+    wkv_end = min(wkv_end, min(qw0 + 32, Lq));
   }
   if (q0 >= Lq) kv_end = 0;
   if (qw0 >= Lq) wkv_end = 0;
@@ -130,49 +178,60 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_d64(const SdpaBf16Param
   const __bf16* Kb = reinterpret_cast<const __bf16*>(p.k) + b * p.ks_b + h * p.ks_h;
   const __bf16* Vb = reinterpret_cast<const __bf16*>(p.v) + b * p.vs_b + h * p.vs_h;
 
-  // Q^T operand: lane holds query qi, d = 16*dstep + 8*g + 0..7.  Padded
-  // query rows load zeros so their (discarded) columns stay finite.
-  bf16x8 qf[4];
-  {
-    const bool qvalid = qi < Lq;
-    const __bf16* qrow = Qb + (int64_t)qi * p.qs_n + 8 * g;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (qvalid) raw = *reinterpret_cast<const u32x4*>(qrow + 16 * d);
-      qf[d] = __builtin_bit_cast(bf16x8, raw);
-    }
-  }
+  // Buffer descriptors over this (b, h)'s rows: each range ends with the last
+  // valid row, so loads of rows past the lengths return zeros (zero K/V keep
+  // 0 * V finite where the padding holds NaN; zero Q rows keep discarded
+  // columns finite).  Row strides are >= 64 elements (host-checked).
+  const uint32_t q_bytes = Lq > 0 ? (uint32_t)((int64_t)(Lq - 1) * p.qs_n * 2 + 128) : 0u;
+  const uint32_t k_bytes = Lkv > 0 ? (uint32_t)((int64_t)(Lkv - 1) * p.ks_n * 2 + 128) : 0u;
+  const uint32_t v_bytes = Lkv > 0 ? (uint32_t)((int64_t)(Lkv - 1) * p.vs_n * 2 + 128) : 0u;
+  const i32x4 rs_q = make_rsrc(Qb, q_bytes);
+  const i32x4 rs_k = make_rsrc(Kb, k_bytes);
+  const i32x4 rs_v = make_rsrc(Vb, v_bytes);
 
-  // Staging: chunk c of a 64x64 tile is row c/8, columns 8*(c%8)..+7.
-  // Key rows at or beyond the length are zero-filled, never read: zero
-  // values keep 0 * V finite even where the padding holds NaN.
-  u32x4 kr[CPT], vr[CPT];
-  auto load_tile = [&](int blk) {
+  // DMA of key tile t into stage t % NS: instruction u of the tile covers row
+  // block u & 7 of K (u < 8) or V (u >= 8); lane l fills row 8*(u&7) + l/8 at
+  // chunk position l%8 with the global chunk that the swizzle maps there.
+  auto issue_tile = [&](int t) {
 #pragma unroll
-    for (int t = 0; t < CPT; ++t) {
-      const int c = tid + t * NT;
-      const int row = c >> 3, col = (c & 7) * 8;
-      const int j = blk * BN + row;
-      if (j < Lkv) {
-        kr[t] = *reinterpret_cast<const u32x4*>(Kb + (int64_t)j * p.ks_n + col);
-        vr[t] = *reinterpret_cast<const u32x4*>(Vb + (int64_t)j * p.vs_n + col);
-      } else {
-        kr[t] = u32x4{0u, 0u, 0u, 0u};
-        vr[t] = u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int i = 0; i < IPT; ++i) {
+      const int u = wave * IPT + i;
+      const bool is_v = u >= 8;
+      const int r = 8 * (u & 7) + (lane >> 3);
+      const int chunk = (lane & 7) ^ (is_v ? swz_v(r) : swz_k(r));
+      const int64_t stride = is_v ? p.vs_n : p.ks_n;
+      const uint32_t voff = (uint32_t)(((int64_t)(t * BN + r) * stride + chunk * 8) * 2);
+      const __bf16* dst = smem + (t % NS) * 2 * TILE_E + (is_v ? TILE_E : 0) + (u & 7) * 512;
+      dma16(voff, is_v ? rs_v : rs_k, lds_addr(dst));
     }
   };
-  auto store_tile = [&](int buf) {
-    __bf16* Ks = smem + buf * 2 * TILE;
+
+  // Q: each wave copies its 32 query rows (4 KiB) into the last ring stage,
+  // which the prologue leaves free; the first in-loop refill of that stage
+  // comes after every wave has read its Q fragments (barrier at blk = 0).
+  const __bf16* Qs = smem + (NS - 1) * 2 * TILE_E + wave * 32 * D;
 #pragma unroll
-    for (int t = 0; t < CPT; ++t) {
-      const int c = tid + t * NT;
-      const int row = c >> 3, col = (c & 7) * 8;
-      *reinterpret_cast<u32x4*>(Ks + row * LDS_ROW + col) = kr[t];
-      *reinterpret_cast<u32x4*>(Ks + TILE + row * LDS_ROW + col) = vr[t];
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * i + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz_k(r);
+    const uint32_t voff = (uint32_t)(((int64_t)(qw0 + r) * p.qs_n + chunk * 8) * 2);
+    dma16(voff, rs_q, lds_addr(Qs + 8 * i * D));
+  }
+  int prologue = 0;
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < nblk) {
+      issue_tile(t);
+      ++prologue;
     }
-  };
+  // Q^T operand: lane holds query qi, d = 16*dstep + 8*g + 0..7
+  wait_vmcnt_le<IPT>(prologue * IPT);
+  bf16x8 qf[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int c = 2 * d + g;
+    qf[d] = *reinterpret_cast<const bf16x8*>(Qs + i32 * D + 8 * (c ^ swz_k(i32)));
+  }
 
   f32x16 o0 = {}, o1 = {};     // O^T for value columns 0..31 and 32..63
   float m = -INFINITY;         // running max of scale*log2(e)*score
@@ -183,29 +242,27 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_d64(const SdpaBf16Param
   const int k16 = lane & 15;
   const int chalf = (lane >> 4) & 1;
   const int tr_row = g * 4 + (k16 >> 2);
-  const int tr_col = chalf * 16 + 4 * (k16 & 3);
-
-  if (nblk > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
+  const int tr_chunk = 2 * chalf + ((k16 & 3) >> 1);   // + 4*cb
+  const int tr_half = 4 * (k16 & 1);                   // element offset inside the chunk
 
   for (int blk = 0; blk < nblk; ++blk) {
-    const int buf = blk & 1;
-    if (blk + 1 < nblk) load_tile(blk + 1);
+    // tile blk has landed once at most min(NS-2, nblk-1-blk) newer tiles are in flight
+    wait_vmcnt_le<IPT>(min(NS - 2, nblk - 1 - blk) * IPT);
+    barrier_lds();  // tile blk visible to all waves; stage (blk-1)%NS free again
+    if (blk + NS - 1 < nblk) issue_tile(blk + NS - 1);
     const int key0 = blk * BN;
 
     if (key0 < wkv_end) {  // wave-uniform: skip tiles entirely after this wave's queries
-      const __bf16* Ks = smem + buf * 2 * TILE;
-      const __bf16* Vs = Ks + TILE;
+      const __bf16* Ks = smem + (blk % NS) * 2 * TILE_E;
+      const __bf16* Vs = Ks + TILE_E;
 
       // S^T = K . Q^T : s0 keys 0..31 of the tile, s1 keys 32..63
       f32x16 s0 = {}, s1 = {};
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + i32 * LDS_ROW + 16 * d + 8 * g);
-        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Ks + (32 + i32) * LDS_ROW + 16 * d + 8 * g);
+        const int c = 2 * d + g;
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + i32 * D + 8 * (c ^ swz_k(i32)));
+        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Ks + (32 + i32) * D + 8 * (c ^ swz_k(32 + i32)));
         s0 = mfma32(ka, qf[d], s0);
         s1 = mfma32(kb, qf[d], s1);
       }
@@ -261,21 +318,22 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_d64(const SdpaBf16Param
       for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const __bf16* vrow = Vs + (32 * jb + 16 * s + tr_row) * LDS_ROW + tr_col;
-          const bf16x4 a0lo = tr_read(vrow);
-          const bf16x4 a0hi = tr_read(vrow + 8 * LDS_ROW);
-          const bf16x4 a1lo = tr_read(vrow + 32);
-          const bf16x4 a1hi = tr_read(vrow + 8 * LDS_ROW + 32);
-          const bf16x8 va0 = __builtin_shufflevector(a0lo, a0hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          const bf16x8 va1 = __builtin_shufflevector(a1lo, a1hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          bf16x4 part[2][2];  // [cb][lo/hi rows]
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int row = 32 * jb + 16 * s + 8 * hh + tr_row;
+            const __bf16* vrow = Vs + row * D + tr_half;
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+              part[cb][hh] = tr_read(vrow + 8 * ((4 * cb + tr_chunk) ^ swz_v(row)));
+          }
+          const bf16x8 va0 = __builtin_shufflevector(part[0][0], part[0][1], 0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x8 va1 = __builtin_shufflevector(part[1][0], part[1][1], 0, 1, 2, 3, 4, 5, 6, 7);
           o0 = mfma32(va0, pf[jb][s], o0);
           o1 = mfma32(va1, pf[jb][s], o1);
         }
       }
     }
-
-    if (blk + 1 < nblk) store_tile(buf ^ 1);
-    __syncthreads();
   }
 
   // epilogue: O = O^T / l, rounded once to bf16; rows without a legal key or
@@ -316,7 +374,7 @@ hipError_t launch_sdpa_bf16(const SdpaBf16Params& p_in, hipStream_t stream) {
   p.n_qblocks = (p.n_q + bm - 1) / bm;
   const int64_t grid = (int64_t)p.n_qblocks * p.batch * p.heads;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(sdpa_fwd_bf16_d64<4>, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((sdpa_fwd_bf16_d64<4, 4>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -83,12 +83,15 @@ typedef struct {
  *   batch, heads >= 1; n_q, n_kv >= 0
  *   d_k, d_v    bf16: d_k = d_v = 64.  f32: 1 <= d_k, d_v <= 64.
  *   sq, sk, sv, so  element strides (NULL = contiguous); bf16 needs every
- *               stride and base pointer 16-byte aligned; f32 needs 4 bytes.
+ *               stride and base pointer 16-byte aligned, row (n) strides of
+ *               Q, K, V >= 64 elements (when that n > 1), and each (batch,
+ *               head) slice of Q, K, V below 2 GiB; f32 needs 4-byte alignment.
  *   scale       0 means 1/sqrt(d_k); otherwise must be finite and > 0.
  *   mask        ATTN_MASK_NONE or ATTN_MASK_CAUSAL.
  *   seqlens_q   device int32 [batch] or NULL.
  *   seqlens_kv  device int32 [batch] or NULL.
  *   lse         device fp32 [batch*heads*n_q] or NULL.
+ * q and o may be NULL when n_q = 0; k and v may be NULL when n_kv = 0.
  * Returns ATTN_OK or a negative attn_status.  o must not alias q, k or v.
  */
 int attn_sdpa_fwd(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k, int d_v,

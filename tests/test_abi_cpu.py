@@ -55,6 +55,8 @@ def sdpa_call(dt=1, B=2, H=2, nq=8, nkv=8, dk=64, dv=64, q=FAKE, k=FAKE, v=FAKE,
     (dict(nq=-1), -1),
     (dict(dk=0), -1),
     (dict(q=None), -1),
+    (dict(k=None), -1),
+    (dict(nkv=0, k=None, v=None, dk=32), -2),  # null K/V allowed when empty
     (dict(o=None), -1),
     (dict(scale=-1.0), -1),
     (dict(scale=float("inf")), -1),
