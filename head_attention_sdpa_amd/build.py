@@ -24,6 +24,9 @@ ARCH = "gfx950"
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs (gfx950 allows it): no AGPR<->VGPR copies
+    # around the softmax and the rescaling of the output accumulator
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 
@@ -39,8 +42,8 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def _compile(src: str, cc: str, extra: list[str]) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+def _compile(src: str, cc: str, extra: list[str], build_dir: str = BUILD_DIR) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     cmd = [cc, *COMMON, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -48,23 +51,27 @@ def _compile(src: str, cc: str, extra: list[str]) -> str:
     return obj
 
 
-def build(extra: list[str] | None = None, verbose: bool = False) -> str:
-    """Compile every source and link LIB_PATH.  Always recompiles."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(extra: list[str] | None = None, verbose: bool = False, out: str | None = None) -> str:
+    """Compile every source and link the library (LIB_PATH unless `out` is
+    given, e.g. for a tuning variant built with extra -D flags).  Always
+    recompiles."""
+    build_dir = BUILD_DIR if out is None else os.path.join(BUILD_DIR, os.path.basename(out))
+    os.makedirs(build_dir, exist_ok=True)
     cc = hipcc()
     extra = list(extra or [])
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, cc, extra), srcs))
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
+        objs = list(ex.map(lambda s: _compile(s, cc, extra, build_dir), srcs))
+    target = LIB_PATH if out is None else out
+    tmp = target + f".tmp{os.getpid()}"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, target)
     if verbose:
-        print(f"built {LIB_PATH} from {len(srcs)} sources")
-    return LIB_PATH
+        print(f"built {target} from {len(srcs)} sources")
+    return target
 
 
 if __name__ == "__main__":

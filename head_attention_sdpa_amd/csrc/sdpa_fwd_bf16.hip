@@ -41,6 +41,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -143,7 +145,7 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_d64(const SdpaBf16Param
   constexpr int BM = 32 * NW;            // queries per workgroup
   constexpr int TILE_E = BN * D;         // bf16 elements per K or V tile (8 KiB)
   constexpr int IPT = 16 / NW;           // DMA instructions per wave per stage (8 K + 8 V row blocks)
-  static_assert(IPT * NW == 16 && NS >= 2, "bad configuration");
+  static_assert(IPT * NW == 16 && NS >= 3, "bad configuration");
   static_assert(NW * 32 * D <= 2 * TILE_E, "the Q rows must fit in one ring stage");
   __shared__ __attribute__((aligned(1024))) __bf16 smem[NS * 2 * TILE_E];  // [stage][K, V][64][64]
 
@@ -186,23 +188,32 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_d64(const SdpaBf16Param
   const uint32_t k_bytes = Lkv > 0 ? (uint32_t)((int64_t)(Lkv - 1) * p.ks_n * 2 + 128) : 0u;
   const uint32_t v_bytes = Lkv > 0 ? (uint32_t)((int64_t)(Lkv - 1) * p.vs_n * 2 + 128) : 0u;
   const i32x4 rs_q = make_rsrc(Qb, q_bytes);
-  const i32x4 rs_k = make_rsrc(Kb, k_bytes);
-  const i32x4 rs_v = make_rsrc(Vb, v_bytes);
 
   // DMA of key tile t into stage t % NS: instruction u of the tile covers row
   // block u & 7 of K (u < 8) or V (u >= 8); lane l fills row 8*(u&7) + l/8 at
   // chunk position l%8 with the global chunk that the swizzle maps there.
+  // Each lane's byte offset inside a tile is fixed; the tile advance moves
+  // the (scalar) descriptor base and shrinks its range, so the range check
+  // keeps zero-filling the rows past the key length.
+  uint32_t dma_off[IPT];
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const int u = wave * IPT + i;
+    const bool is_v = u >= 8;
+    const int r = 8 * (u & 7) + (lane >> 3);
+    const int chunk = (lane & 7) ^ (is_v ? swz_v(r) : swz_k(r));
+    dma_off[i] = (uint32_t)(((int64_t)r * (is_v ? p.vs_n : p.ks_n) + chunk * 8) * 2);
+  }
   auto issue_tile = [&](int t) {
+    const int64_t k_adv = (int64_t)t * BN * p.ks_n, v_adv = (int64_t)t * BN * p.vs_n;
+    const i32x4 rk = make_rsrc(Kb + k_adv, (uint32_t)max<int64_t>(0, (int64_t)k_bytes - 2 * k_adv));
+    const i32x4 rv = make_rsrc(Vb + v_adv, (uint32_t)max<int64_t>(0, (int64_t)v_bytes - 2 * v_adv));
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
       const int u = wave * IPT + i;
       const bool is_v = u >= 8;
-      const int r = 8 * (u & 7) + (lane >> 3);
-      const int chunk = (lane & 7) ^ (is_v ? swz_v(r) : swz_k(r));
-      const int64_t stride = is_v ? p.vs_n : p.ks_n;
-      const uint32_t voff = (uint32_t)(((int64_t)(t * BN + r) * stride + chunk * 8) * 2);
       const __bf16* dst = smem + (t % NS) * 2 * TILE_E + (is_v ? TILE_E : 0) + (u & 7) * 512;
-      dma16(voff, is_v ? rs_v : rs_k, lds_addr(dst));
+      dma16(dma_off[i], is_v ? rv : rk, lds_addr(dst));
     }
   };
 
@@ -245,95 +256,142 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_d64(const SdpaBf16Param
   const int tr_chunk = 2 * chalf + ((k16 & 3) >> 1);   // + 4*cb
   const int tr_half = 4 * (k16 & 1);                   // element offset inside the chunk
 
-  for (int blk = 0; blk < nblk; ++blk) {
-    // tile blk has landed once at most min(NS-2, nblk-1-blk) newer tiles are in flight
-    wait_vmcnt_le<IPT>(min(NS - 2, nblk - 1 - blk) * IPT);
-    barrier_lds();  // tile blk visible to all waves; stage (blk-1)%NS free again
-    if (blk + NS - 1 < nblk) issue_tile(blk + NS - 1);
+  // S^T = K_tile . Q^T for the tile in `stage`: s0 keys 0..31, s1 keys 32..63
+  auto qk = [&](int stage, f32x16& s0, f32x16& s1) {
+    const __bf16* Ks = smem + stage * 2 * TILE_E;
+    s0 = f32x16{};
+    s1 = f32x16{};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int c = 2 * d + g;
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + i32 * D + 8 * (c ^ swz_k(i32)));
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Ks + (32 + i32) * D + 8 * (c ^ swz_k(32 + i32)));
+      s0 = mfma32(ka, qf[d], s0);
+      s1 = mfma32(kb, qf[d], s1);
+    }
+  };
+
+  // One iteration of the software pipeline.  The softmax and P.V of tile blk
+  // run in four blocks of 16 keys; between them the wave issues one d-step
+  // (two MFMAs) of the Q.K^T products of tile blk+1 (into sn) and the two
+  // P.V MFMAs of the block just computed.  Every MFMA is thus separated from
+  // the one it depends on by a block of vector work, so the matrix cores run
+  // the next tile's scores and this tile's P.V while the vector ALUs run the
+  // softmax.  The loop below is unrolled by two with the score buffers
+  // swapping roles, so no registers are copied between iterations.
+  auto step = [&](int blk, f32x16& sc0, f32x16& sc1, f32x16& sn0, f32x16& sn1) {
     const int key0 = blk * BN;
-
-    if (key0 < wkv_end) {  // wave-uniform: skip tiles entirely after this wave's queries
-      const __bf16* Ks = smem + (blk % NS) * 2 * TILE_E;
-      const __bf16* Vs = Ks + TILE_E;
-
-      // S^T = K . Q^T : s0 keys 0..31 of the tile, s1 keys 32..63
-      f32x16 s0 = {}, s1 = {};
+    bool do_next = false;
+    if (blk + 1 < nblk) {
+      // tile blk+1 has landed once at most min(NS-3, nblk-2-blk) newer tiles are in flight
+      wait_vmcnt_le<IPT>(min(NS - 3, nblk - 2 - blk) * IPT);
+      barrier_lds();  // tile blk+1 visible; every wave is past P.V of tile blk-1
+      if (blk + NS - 1 < nblk) issue_tile(blk + NS - 1);  // into the stage of tile blk-1
+      do_next = key0 + BN < wkv_end;
+    }
+    const __bf16* Kn = smem + ((blk + 1) % NS) * 2 * TILE_E;
+    // one d-step of S^T(next) = K_next . Q^T
+    auto qk_step = [&](int d) {
+      const int c = 2 * d + g;
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Kn + i32 * D + 8 * (c ^ swz_k(i32)));
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Kn + (32 + i32) * D + 8 * (c ^ swz_k(32 + i32)));
+      sn0 = mfma32(ka, qf[d], d == 0 ? f32x16{} : sn0);
+      sn1 = mfma32(kb, qf[d], d == 0 ? f32x16{} : sn1);
+    };
+    if (key0 >= wkv_end) {  // wave-uniform: tile entirely after this wave's queries
+      if (do_next)
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const int c = 2 * d + g;
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + i32 * D + 8 * (c ^ swz_k(i32)));
-        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Ks + (32 + i32) * D + 8 * (c ^ swz_k(32 + i32)));
-        s0 = mfma32(ka, qf[d], s0);
-        s1 = mfma32(kb, qf[d], s1);
-      }
+        for (int d = 0; d < 4; ++d) qk_step(d);
+      return;
+    }
+    const __bf16* Vs = smem + (blk % NS) * 2 * TILE_E + TILE_E;
 
-      // -inf for illegal keys: only the tiles that cross the length or the diagonal
-      if (key0 + BN > Lkv || (p.causal && key0 + BN - 1 > qw0)) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j0 = key0 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const int j1 = j0 + 32;
-          if (j0 >= Lkv || (p.causal && j0 > qi)) s0[r] = -INFINITY;
-          if (j1 >= Lkv || (p.causal && j1 > qi)) s1[r] = -INFINITY;
-        }
-      }
-
-      // online softmax
-      float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-      mx = max_with_partner(mx);
-      const float m_new = fmaxf(m, mx * c2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // no legal key yet: avoid -inf - -inf
-      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-      float rs = 0.f;
+    // -inf for illegal keys (only tiles that cross the length or the
+    // diagonal): key key0 + pos is legal iff pos <= thr, where the lane's
+    // register r holds pos = 8*(r/4) + 4*g + r%4 (+32 in sc1)
+    if (key0 + BN > Lkv || (p.causal && key0 + BN - 1 > qw0)) {
+      const int lim = p.causal ? min(Lkv - 1, qi) : Lkv - 1;
+      const int thr = lim - key0 - 4 * g;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], c2, -m_use));
-        s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], c2, -m_use));
-        rs += s0[r] + s1[r];
+        const int pos = 8 * (r >> 2) + (r & 3);
+        if (pos > thr) sc0[r] = -INFINITY;
+        if (pos + 32 > thr) sc1[r] = -INFINITY;
       }
-      l = fmaf(l, alpha, rs);
-      m = m_new;
+    }
+
+    // online softmax.  A lane's running max m is only moved (and its O, l
+    // rescaled) when its tile max exceeds m by more than 8 (log2 units):
+    // otherwise the stale m stays the shift, which the softmax is invariant
+    // to, and the weights stay below 2^8.  The decision is per lane, so a
+    // query's arithmetic never depends on the other queries of the wave.
+    float mx = fmaxf(sc0[0], sc1[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, sc0[r]), sc1[r]);
+    mx = max_with_partner(mx) * c2;
+    const bool grow = mx > m + 8.f;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform skip; per-lane decision
+      const float m_new = grow ? mx : m;     // lanes that do not grow keep m: alpha = 1 exactly
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // m = -inf: alpha = 0
+      l *= alpha;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         o0[r] *= alpha;
         o1[r] *= alpha;
       }
-
-      // P^T operands: step (jb, s) covers keys 32*jb + 16*s + 0..15; lane's
-      // element t is key 32*jb + 16*s + 8*(t/4) + 4*g + t%4 (the C layout).
-      bf16x8 pf[2][2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          pf[0][s][t] = (__bf16)s0[8 * s + t];
-          pf[1][s][t] = (__bf16)s1[8 * s + t];
-        }
-      }
-
-      // O^T += V^T . P^T ; the A operand for (cb, jb, s) is V[key(t)][32*cb + lane%32]
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          bf16x4 part[2][2];  // [cb][lo/hi rows]
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int row = 32 * jb + 16 * s + 8 * hh + tr_row;
-            const __bf16* vrow = Vs + row * D + tr_half;
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
-              part[cb][hh] = tr_read(vrow + 8 * ((4 * cb + tr_chunk) ^ swz_v(row)));
-          }
-          const bf16x8 va0 = __builtin_shufflevector(part[0][0], part[0][1], 0, 1, 2, 3, 4, 5, 6, 7);
-          const bf16x8 va1 = __builtin_shufflevector(part[1][0], part[1][1], 0, 1, 2, 3, 4, 5, 6, 7);
-          o0 = mfma32(va0, pf[jb][s], o0);
-          o1 = mfma32(va1, pf[jb][s], o1);
-        }
-      }
+      m = m_new;
     }
+    const float m_use = (m == -INFINITY) ? 0.f : m;  // no legal key yet: avoid -inf - -inf
+
+    // Blocks (jb, s) cover keys 32*jb + 16*s + 0..15.  The P^T operand's
+    // element t is key 32*jb + 16*s + 8*(t/4) + 4*g + t%4 (the C layout of
+    // the scores); the row sum adds the bf16-rounded weights (the ones P.V
+    // uses), two per instruction with a dot product against (1, 1).  The V^T
+    // operand for (cb, jb, s) is V[key(t)][32*cb + lane%32], read transposed.
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+    float rs = 0.f;
+#pragma unroll
+    for (int blkq = 0; blkq < 4; ++blkq) {
+      const int jb = blkq >> 1, s = blkq & 1;
+      const f32x16& sc = jb ? sc1 : sc0;
+      bf16x4 part[2][2];  // [cb][lo/hi rows]
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int row = 32 * jb + 16 * s + 8 * hh + tr_row;
+        const __bf16* vrow = Vs + row * D + tr_half;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+          part[cb][hh] = tr_read(vrow + 8 * ((4 * cb + tr_chunk) ^ swz_v(row)));
+      }
+      bf16x2 pp[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const f32x2 e = {__builtin_amdgcn_exp2f(fmaf(sc[8 * s + 2 * t], c2, -m_use)),
+                         __builtin_amdgcn_exp2f(fmaf(sc[8 * s + 2 * t + 1], c2, -m_use))};
+        pp[t] = __builtin_convertvector(e, bf16x2);
+        rs = __builtin_amdgcn_fdot2_f32_bf16(pp[t], ones, rs, false);
+      }
+      if (do_next) qk_step(blkq);
+      const bf16x8 pf = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+                                                __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
+                                                0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 va0 = __builtin_shufflevector(part[0][0], part[0][1], 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 va1 = __builtin_shufflevector(part[1][0], part[1][1], 0, 1, 2, 3, 4, 5, 6, 7);
+      o0 = mfma32(va0, pf, o0);
+      o1 = mfma32(va1, pf, o1);
+    }
+    l += rs;
+  };
+
+  f32x16 sa0 = {}, sa1 = {}, sb0 = {}, sb1 = {};
+  if (nblk > 0) {
+    wait_vmcnt_le<IPT>(min(NS - 2, nblk - 1) * IPT);   // tile 0 landed
+    barrier_lds();
+    if (0 < wkv_end) qk(0, sa0, sa1);
+  }
+  for (int blk = 0; blk < nblk; blk += 2) {
+    step(blk, sa0, sa1, sb0, sb1);
+    if (blk + 1 < nblk) step(blk + 1, sb0, sb1, sa0, sa1);
   }
 
   // epilogue: O = O^T / l, rounded once to bf16; rows without a legal key or
@@ -368,13 +426,28 @@ int sdpa_bf16_block_m(int batch, int heads, int n_q) {
   return 128;
 }
 
+// Ring depth: with up to 5 key tiles (n_kv <= 320) a 5-stage ring puts every
+// tile of the workgroup in flight at once (one memory round trip); longer
+// sequences use 4 stages (64 KiB, two workgroups per CU).
+#ifndef ATTN_SDPA_NS_SHORT
+#define ATTN_SDPA_NS_SHORT 5
+#endif
+#ifndef ATTN_SDPA_NS_LONG
+#define ATTN_SDPA_NS_LONG 4
+#endif
+
 hipError_t launch_sdpa_bf16(const SdpaBf16Params& p_in, hipStream_t stream) {
   SdpaBf16Params p = p_in;
   const int bm = sdpa_bf16_block_m(p.batch, p.heads, p.n_q);
   p.n_qblocks = (p.n_q + bm - 1) / bm;
   const int64_t grid = (int64_t)p.n_qblocks * p.batch * p.heads;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((sdpa_fwd_bf16_d64<4, 4>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+  if (p.n_kv <= 64 * (ATTN_SDPA_NS_SHORT - 1) + 64)
+    hipLaunchKernelGGL((sdpa_fwd_bf16_d64<4, ATTN_SDPA_NS_SHORT>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((sdpa_fwd_bf16_d64<4, ATTN_SDPA_NS_LONG>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, p);
   return hipGetLastError();
 }
 

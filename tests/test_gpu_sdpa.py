@@ -14,7 +14,10 @@ from gpu_helpers import announce, lens_gpu, max_err, to_f64, to_gpu
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
-LSE_TOL = {"f32": 1e-4, "bf16": 1e-3}
+# bf16 path: the softmax denominator sums the bf16-rounded weights (the ones
+# that enter P.V), each within a relative 2^-9 of its fp32 value, so
+# |d ln l| <= 2^-9 / (1 - 2^-9) ~ 2e-3; 4e-3 leaves room for fp32 score rounding.
+LSE_TOL = {"f32": 1e-4, "bf16": 4e-3}
 
 
 def attn_mod():
