@@ -286,6 +286,22 @@ def cpu_baseline(cfg_id, inp, flops_full):
             "sample": sample, "seconds": dt}
 
 
+def calibrate_copy(K):
+    """A plain device copy of known size (256 MiB read, 256 MiB written), run
+    eagerly K times: the reference that hardware byte counters (FETCH_SIZE,
+    WRITE_SIZE) are scaled by, and the achievable HBM copy rate."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = 256 << 20
+    a = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ms = time_eager(lambda s: b.copy_(a), K, torch)
+    return {"calibration": "device copy", "bytes_read": n, "bytes_written": n, "launches": K + 1,
+            "ms_per_copy": ms, "copy_GBs": 2 * n / (ms * 1e-3) / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -294,6 +310,8 @@ def main():
     ap.add_argument("--workload", default="decoder", choices=sorted(WORKLOAD_CFG))
     ap.add_argument("--hot", action="store_true", help="reuse one input set (cache-hot)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="time a 256 MiB device copy instead (byte-counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -303,6 +321,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        print(json.dumps(calibrate_copy(args.steps)), flush=True)
+        return
     cfg_id = WORKLOAD_CFG[args.workload]
     K, W = args.steps, args.warmup
     if cfg_id == 5:

@@ -172,10 +172,211 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(const GemmBf16Params p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Main kernel for the common shapes (column panels a multiple of 128 wide,
+// K a multiple of 64): workgroup tile 256 (m) x 128 (n) x 64 (k), four waves
+// in a 2 x 2 arrangement of 128 (m) x 64 (n) wave tiles (8 MFMA accumulators
+// per wave: 8 MFMAs per 4 + 4 LDS reads).  X and W tiles are copied global ->
+// LDS by buffer_load ... lds into a 3-stage ring; rows past M read as zeros
+// from the buffer range.  LDS layouts are XOR-swizzled (no padding):
+//   X tile [256 m][64 k]: 16-byte chunk c of row r at position c ^ ((r>>1)&7)
+//     (16 consecutive rows read one chunk each: distinct banks)
+//   W tile [64 k][128 n]: chunk c of row r at position c ^ (4*(r&3))
+//     (transposed reads touch 4 consecutive rows x 2 or 4 chunks)
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  // the descriptor must live in scalar registers: all inputs are wave-uniform
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+__device__ __forceinline__ void dma16(uint32_t voff, i32x4 rsrc, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               ::"v"(voff), "s"(rsrc), "s"(lds_addr) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>(p);
+}
+
+constexpr int M2 = 256, N2 = 128, K2 = 64, S2 = 3;
+constexpr int X_TILE = M2 * K2;          // bf16 elements (32 KiB)
+constexpr int W_TILE = K2 * N2;          // 16 KiB
+constexpr int STAGE2 = X_TILE + W_TILE;
+constexpr int IPW = (X_TILE + W_TILE) * 2 / 1024 / 4;  // DMA instructions per wave per stage (12)
+
+__device__ __forceinline__ int swz_x(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz_w(int r) { return 4 * (r & 3); }
+
+__global__ __launch_bounds__(256) void gemm_bf16_dma_kernel(const GemmBf16Params p) {
+  __shared__ __attribute__((aligned(1024))) __bf16 smem[S2 * STAGE2];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int wm = wave & 1, wn = wave >> 1;   // wave tile: rows 128*wm.., cols 64*wn..
+
+  constexpr int GM = 8;
+  const int tiles_m = (p.M + M2 - 1) / M2;
+  const int tiles_n = p.N / N2;
+  const int total = tiles_m * tiles_n;
+  int tile = blockIdx.x;
+  if ((total & 7) == 0) tile = (tile & 7) * (total >> 3) + (tile >> 3);
+  const int grp = tile / (GM * tiles_n);
+  const int rem = tile - grp * (GM * tiles_n);
+  const int gm_here = min(GM, tiles_m - grp * GM);
+  const int tn = rem / gm_here, tm = grp * GM + (rem - (rem / gm_here) * gm_here);
+  const int m0 = tm * M2, n0 = tn * N2;
+
+  // descriptors: X rows m0.. (rows >= M read as zeros); W panel columns n0..
+  const __bf16* Xb = reinterpret_cast<const __bf16*>(p.a) + (int64_t)m0 * p.lda;
+  const int rows_here = min(M2, p.M - m0);
+  const uint32_t x_bytes = (uint32_t)((int64_t)(rows_here - 1) * p.lda * 2 + (int64_t)p.K * 2);
+  const int panel = n0 / p.n_panel;
+  // (explicit selection keeps the kernel-argument array in scalar registers)
+  const uint16_t* wpanel = panel == 0 ? p.b[0] : (panel == 1 ? p.b[1] : p.b[2]);
+  const __bf16* Wb = reinterpret_cast<const __bf16*>(wpanel) + (n0 - panel * p.n_panel);
+  const uint32_t w_bytes = (uint32_t)((int64_t)(p.K - 1) * p.n_panel * 2 + N2 * 2);
+
+  // per-lane DMA offsets (relative to the k-tile base)
+  uint32_t off[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int u = wave * IPW + i;        // 0..31 X row blocks (8 rows), 32..47 W row blocks (4 rows)
+    if (u < 32) {
+      const int r = 8 * u + (lane >> 3);
+      const int c = (lane & 7) ^ swz_x(r);
+      off[i] = (uint32_t)(((int64_t)r * p.lda + c * 8) * 2);
+    } else {
+      const int r = 4 * (u - 32) + (lane >> 4);
+      const int c = (lane & 15) ^ swz_w(r);
+      off[i] = (uint32_t)(((int64_t)r * p.n_panel + c * 8) * 2);
+    }
+  }
+  const int nk = p.K / K2;
+  auto issue = [&](int kt) {
+    const i32x4 rx = make_rsrc(Xb + kt * K2, x_bytes > (uint32_t)(kt * K2 * 2) ? x_bytes - kt * K2 * 2 : 0u);
+    const i32x4 rw = make_rsrc(Wb + (int64_t)kt * K2 * p.n_panel,
+                               (uint32_t)((int64_t)w_bytes - (int64_t)kt * K2 * p.n_panel * 2));
+    __bf16* st = smem + (kt % S2) * STAGE2;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int u = wave * IPW + i;   // wave-uniform: selects, no branches
+      const bool x = u < 32;
+      dma16(off[i], x ? rx : rw, lds_addr(st + (x ? u * 512 : X_TILE + (u - 32) * 512)));
+    }
+  };
+
+  f32x16 acc[2][4] = {};   // [n block][m block]
+
+  const int k16 = lane & 15, chalf = (lane >> 4) & 1;
+  const int tr_row = g * 8 + (k16 >> 2);           // + 16*ks (+4 for the second half)
+  const int tr_chunk = 2 * chalf + ((k16 & 3) >> 1);  // + 4*nb + 8*wn
+  const int tr_half = 4 * (k16 & 1);
+
+  // fragments of one 16-wide k-step: X rows (MFMA B operand) and W^T rows
+  // (MFMA A operand, transposed reads of the row-major W tile)
+  auto load_frags = [&](int kt, int ks, bf16x8 (&xf)[4], bf16x8 (&wf)[2]) {
+    const __bf16* Xs = smem + (kt % S2) * STAGE2;
+    const __bf16* Ws = Xs + X_TILE;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int r = wm * 128 + mb * 32 + l32;
+      const int c = 2 * ks + g;
+      xf[mb] = *reinterpret_cast<const bf16x8*>(Xs + r * K2 + 8 * (c ^ swz_x(r)));
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int c = 8 * wn + 4 * nb + tr_chunk;
+      const int r0 = 16 * ks + tr_row, r1 = r0 + 4;
+      const bf16x4 lo = tr_read(Ws + r0 * N2 + 8 * (c ^ swz_w(r0)) + tr_half);
+      const bf16x4 hi = tr_read(Ws + r1 * N2 + 8 * (c ^ swz_w(r1)) + tr_half);
+      wf[nb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+
+  // Prologue: all three ring stages in flight.  In the loop, the fragments of
+  // the next k-step are read before the MFMAs of the current one; the
+  // k-tile barrier sits inside the last k-step, after every fragment of the
+  // tile is in registers, so it also frees that tile's stage for the tile
+  // three ahead (two tiles stay in flight).
+  int pro = 0;
+#pragma unroll
+  for (int t = 0; t < S2; ++t)
+    if (t < nk) {
+      issue(t);
+      ++pro;
+    }
+  if (pro >= 3) wait_vmcnt<2 * IPW>();
+  else if (pro == 2) wait_vmcnt<IPW>();
+  else wait_vmcnt<0>();
+  barrier_lds();
+  bf16x8 xa[4], wa[2], xb[4], wb[2];
+  load_frags(0, 0, xa, wa);
+  auto mfmas = [&](const bf16x8 (&xf)[4], const bf16x8 (&wf)[2]) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma32(wf[nb], xf[mb], acc[nb][mb]);
+  };
+  for (int kt = 0; kt < nk; ++kt) {
+    load_frags(kt, 1, xb, wb);
+    mfmas(xa, wa);
+    load_frags(kt, 2, xa, wa);
+    mfmas(xb, wb);
+    load_frags(kt, 3, xb, wb);
+    mfmas(xa, wa);
+    if (kt + 1 < nk) {
+      // tile kt+1 landed once at most min(1, nk-2-kt) newer tiles are in flight
+      if (kt + 2 < nk) wait_vmcnt<IPW>(); else wait_vmcnt<0>();
+      barrier_lds();                     // every wave holds all of tile kt: its stage is free
+      if (kt + S2 < nk) issue(kt + S2);  // into the stage of tile kt
+      load_frags(kt + 1, 0, xa, wa);
+    }
+    mfmas(xb, wb);
+  }
+
+  // acc[nb][mb] register r -> n = n0 + 64*wn + 32*nb + 8*(r/4) + 4*g + r%4,
+  //                           m = m0 + 128*wm + 32*mb + lane%32
+  __bf16* C = reinterpret_cast<__bf16*>(p.c);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int m = m0 + wm * 128 + mb * 32 + l32;
+    if (m >= p.M) continue;
+    __bf16* crow = C + (int64_t)m * p.ldc + n0 + 64 * wn;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        bf16x4 w;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) w[t] = (__bf16)acc[nb][mb][4 * rg + t];
+        *reinterpret_cast<u32x2*>(crow + 32 * nb + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, w);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmBf16Params& p, hipStream_t stream) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
+  // main kernel: whole 128-column tiles inside one panel, K in 64-steps, and
+  // per-tile buffer ranges within 32-bit offsets
+  if (p.n_panel % N2 == 0 && p.N % N2 == 0 && p.K % K2 == 0 &&
+      (int64_t)M2 * p.lda * 2 < 0x7fffffffLL && (int64_t)p.K * p.n_panel * 2 < 0x7fffffffLL) {
+    const int64_t tiles = (int64_t)((p.M + M2 - 1) / M2) * (p.N / N2);
+    hipLaunchKernelGGL(gemm_bf16_dma_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
   const int64_t tiles = (int64_t)((p.M + BM - 1) / BM) * ((p.N + BNt - 1) / BNt);
   hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)tiles), dim3(NT), 0, stream, p);
   return hipGetLastError();

@@ -109,8 +109,11 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // Raw buffer descriptor: 48-bit base, stride 0, range in bytes; reads at or
 // past the range return zeros.
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  // the descriptor must live in scalar registers: all inputs are wave-uniform
   const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32) & 0xffff, (int)bytes, 0x00020000};
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
 }
 
 __device__ __forceinline__ void dma16(uint32_t voff, i32x4 rsrc, uint32_t lds_addr) {
@@ -417,6 +420,240 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_d64(const SdpaBf16Param
   }
 }
 
+// ---------------------------------------------------------------------------
+// Variant with 64 queries per wave (two 32-query column blocks): every K and
+// V fragment read from LDS feeds two MFMAs, which halves the LDS read traffic
+// per MFMA (the transposed V reads are the most expensive LDS operation).
+// Two waves per workgroup (128 queries), same grid as the 32-query kernel.
+// Within a tile the softmax of one query block overlaps the MFMAs of the
+// other: Q.K^T of block 0, Q.K^T of block 1, softmax 0, P.V 0, softmax 1, P.V 1.
+template <int NS>
+__global__ __launch_bounds__(128) void sdpa_fwd_bf16_d64_q64(const SdpaBf16Params p) {
+  constexpr int NW = 2, QB = 2;
+  constexpr int BM = 32 * QB * NW;       // 128 queries per workgroup
+  constexpr int TILE_E = BN * D;
+  constexpr int IPT = 16 / NW;           // 8 DMA instructions per wave per stage
+  static_assert(NS >= 2, "bad configuration");
+  static_assert(NW * QB * 32 * D <= 2 * TILE_E, "the Q rows must fit in one ring stage");
+  __shared__ __attribute__((aligned(1024))) __bf16 smem[NS * 2 * TILE_E];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i32 = lane & 31, g = lane >> 5;
+
+  int bh, qb;
+  map_block(blockIdx.x, p.batch * p.heads, p.n_qblocks, p.causal, bh, qb);
+  const int b = bh / p.heads, h = bh - b * p.heads;
+
+  int Lq = p.n_q, Lkv = p.n_kv;
+  if (p.seqlens_q) Lq = min(max(p.seqlens_q[b], 0), p.n_q);
+  if (p.seqlens_kv) Lkv = min(max(p.seqlens_kv[b], 0), p.n_kv);
+
+  const int q0 = qb * BM;
+  const int qw0 = q0 + wave * 64;         // this wave's 64 queries: qw0 .. qw0+63
+  int qi[QB];
+#pragma unroll
+  for (int c = 0; c < QB; ++c) qi[c] = qw0 + 32 * c + i32;
+
+  int kv_end = Lkv, wkv_end = Lkv;
+  if (p.causal) {
+    kv_end = min(kv_end, min(q0 + BM, Lq));
+    wkv_end = min(wkv_end, min(qw0 + 64, Lq));
+  }
+  if (q0 >= Lq) kv_end = 0;
+  if (qw0 >= Lq) wkv_end = 0;
+  const int nblk = (kv_end + BN - 1) / BN;
+
+  const __bf16* Qb = reinterpret_cast<const __bf16*>(p.q) + b * p.qs_b + h * p.qs_h;
+  const __bf16* Kb = reinterpret_cast<const __bf16*>(p.k) + b * p.ks_b + h * p.ks_h;
+  const __bf16* Vb = reinterpret_cast<const __bf16*>(p.v) + b * p.vs_b + h * p.vs_h;
+  const uint32_t q_bytes = Lq > 0 ? (uint32_t)((int64_t)(Lq - 1) * p.qs_n * 2 + 128) : 0u;
+  const uint32_t k_bytes = Lkv > 0 ? (uint32_t)((int64_t)(Lkv - 1) * p.ks_n * 2 + 128) : 0u;
+  const uint32_t v_bytes = Lkv > 0 ? (uint32_t)((int64_t)(Lkv - 1) * p.vs_n * 2 + 128) : 0u;
+  const i32x4 rs_q = make_rsrc(Qb, q_bytes);
+
+  uint32_t dma_off[IPT];
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const int u = wave * IPT + i;
+    const bool is_v = u >= 8;
+    const int r = 8 * (u & 7) + (lane >> 3);
+    const int chunk = (lane & 7) ^ (is_v ? swz_v(r) : swz_k(r));
+    dma_off[i] = (uint32_t)(((int64_t)r * (is_v ? p.vs_n : p.ks_n) + chunk * 8) * 2);
+  }
+  auto issue_tile = [&](int t) {
+    const int64_t k_adv = (int64_t)t * BN * p.ks_n, v_adv = (int64_t)t * BN * p.vs_n;
+    const i32x4 rk = make_rsrc(Kb + k_adv, (uint32_t)max<int64_t>(0, (int64_t)k_bytes - 2 * k_adv));
+    const i32x4 rv = make_rsrc(Vb + v_adv, (uint32_t)max<int64_t>(0, (int64_t)v_bytes - 2 * v_adv));
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int u = wave * IPT + i;
+      if (u < 8) dma16(dma_off[i], rk, lds_addr(smem + (t % NS) * 2 * TILE_E + u * 512));
+      else dma16(dma_off[i], rv, lds_addr(smem + (t % NS) * 2 * TILE_E + TILE_E + (u - 8) * 512));
+    }
+  };
+
+  // Q: each wave copies its 64 query rows (8 KiB) into the last ring stage
+  const __bf16* Qs = smem + (NS - 1) * 2 * TILE_E + wave * 64 * D;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * i + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz_k(r);
+    const uint32_t voff = (uint32_t)(((int64_t)(qw0 + r) * p.qs_n + chunk * 8) * 2);
+    dma16(voff, rs_q, lds_addr(Qs + 8 * i * D));
+  }
+  int prologue = 0;
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < nblk) {
+      issue_tile(t);
+      ++prologue;
+    }
+  wait_vmcnt_le<IPT>(prologue * IPT);
+  bf16x8 qf[QB][4];
+#pragma unroll
+  for (int c = 0; c < QB; ++c)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int r = 32 * c + i32, ch = 2 * d + g;
+      qf[c][d] = *reinterpret_cast<const bf16x8*>(Qs + r * D + 8 * (ch ^ swz_k(r)));
+    }
+
+  f32x16 o[QB][2] = {};       // O^T[query block][value columns 0..31 / 32..63]
+  float m[QB], l[QB];
+#pragma unroll
+  for (int c = 0; c < QB; ++c) {
+    m[c] = -INFINITY;
+    l[c] = 0.f;
+  }
+  const float c2 = p.scale_log2;
+  const int k16 = lane & 15;
+  const int chalf = (lane >> 4) & 1;
+  const int tr_row = g * 4 + (k16 >> 2);
+  const int tr_chunk = 2 * chalf + ((k16 & 3) >> 1);
+  const int tr_half = 4 * (k16 & 1);
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+
+  for (int blk = 0; blk < nblk; ++blk) {
+    wait_vmcnt_le<IPT>(min(NS - 2, nblk - 1 - blk) * IPT);   // tile blk landed
+    barrier_lds();                                           // stage (blk-1)%NS free
+    if (blk + NS - 1 < nblk) issue_tile(blk + NS - 1);
+    const int key0 = blk * BN;
+    if (key0 >= wkv_end) continue;  // wave-uniform
+    const __bf16* Ks = smem + (blk % NS) * 2 * TILE_E;
+    const __bf16* Vs = Ks + TILE_E;
+
+    // S^T[query block c][key half kb] = K_kb . Q_c^T ; each K fragment feeds both query blocks
+    f32x16 sc[QB][2];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int ch = 2 * d + g;
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + i32 * D + 8 * (ch ^ swz_k(i32)));
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Ks + (32 + i32) * D + 8 * (ch ^ swz_k(32 + i32)));
+#pragma unroll
+      for (int c = 0; c < QB; ++c) {
+        sc[c][0] = mfma32(ka, qf[c][d], d == 0 ? f32x16{} : sc[c][0]);
+        sc[c][1] = mfma32(kb, qf[c][d], d == 0 ? f32x16{} : sc[c][1]);
+      }
+    }
+
+    // softmax of each query block, then P.V with V fragments shared by both blocks
+    bf16x8 pf[QB][4];   // [query block][key block (jb, s) = 2*jb + s]
+#pragma unroll
+    for (int c = 0; c < QB; ++c) {
+      if (key0 + BN > Lkv || (p.causal && key0 + BN - 1 > qw0 + 32 * c)) {
+        const int lim = p.causal ? min(Lkv - 1, qi[c]) : Lkv - 1;
+        const int thr = lim - key0 - 4 * g;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int pos = 8 * (r >> 2) + (r & 3);
+          if (pos > thr) sc[c][0][r] = -INFINITY;
+          if (pos + 32 > thr) sc[c][1][r] = -INFINITY;
+        }
+      }
+      float mx = fmaxf(sc[c][0][0], sc[c][1][0]);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, sc[c][0][r]), sc[c][1][r]);
+      mx = max_with_partner(mx) * c2;
+      const bool grow = mx > m[c] + 8.f;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float m_new = grow ? mx : m[c];
+        const float alpha = __builtin_amdgcn_exp2f(m[c] - m_new);
+        l[c] *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          o[c][0][r] *= alpha;
+          o[c][1][r] *= alpha;
+        }
+        m[c] = m_new;
+      }
+      const float m_use = (m[c] == -INFINITY) ? 0.f : m[c];
+      float rs = 0.f;
+#pragma unroll
+      for (int kbk = 0; kbk < 4; ++kbk) {
+        const int jb = kbk >> 1, s = kbk & 1;
+        bf16x2 pp[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const f32x2 e = {__builtin_amdgcn_exp2f(fmaf(sc[c][jb][8 * s + 2 * t], c2, -m_use)),
+                           __builtin_amdgcn_exp2f(fmaf(sc[c][jb][8 * s + 2 * t + 1], c2, -m_use))};
+          pp[t] = __builtin_convertvector(e, bf16x2);
+          rs = __builtin_amdgcn_fdot2_f32_bf16(pp[t], ones, rs, false);
+        }
+        pf[c][kbk] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+                                             __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
+                                             0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      l[c] += rs;
+    }
+#pragma unroll
+    for (int kbk = 0; kbk < 4; ++kbk) {
+      const int jb = kbk >> 1, s = kbk & 1;
+      bf16x4 part[2][2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int row = 32 * jb + 16 * s + 8 * hh + tr_row;
+        const __bf16* vrow = Vs + row * D + tr_half;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+          part[cb][hh] = tr_read(vrow + 8 * ((4 * cb + tr_chunk) ^ swz_v(row)));
+      }
+      const bf16x8 va0 = __builtin_shufflevector(part[0][0], part[0][1], 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 va1 = __builtin_shufflevector(part[1][0], part[1][1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int c = 0; c < QB; ++c) {
+        o[c][0] = mfma32(va0, pf[c][kbk], o[c][0]);
+        o[c][1] = mfma32(va1, pf[c][kbk], o[c][1]);
+      }
+    }
+  }
+
+  // epilogue per query block
+#pragma unroll
+  for (int c = 0; c < QB; ++c) {
+    const float lt = sum_with_partner(l[c]);
+    if (qi[c] < p.n_q) {
+      const bool valid = (qi[c] < Lq) && (lt > 0.f);
+      const float inv = valid ? 1.f / lt : 0.f;
+      __bf16* orow = reinterpret_cast<__bf16*>(p.o) + b * p.os_b + h * p.os_h + (int64_t)qi[c] * p.os_n;
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        bf16x4 w0, w1;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          w0[t] = (__bf16)(o[c][0][4 * rg + t] * inv);
+          w1[t] = (__bf16)(o[c][1][4 * rg + t] * inv);
+        }
+        *reinterpret_cast<u32x2*>(orow + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, w0);
+        *reinterpret_cast<u32x2*>(orow + 32 + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, w1);
+      }
+      if (p.lse && g == 0)
+        p.lse[((int64_t)b * p.heads + h) * p.n_q + qi[c]] = valid ? (m[c] + __log2f(lt)) * LN2 : -INFINITY;
+    }
+  }
+}
+
 }  // namespace
 
 int sdpa_bf16_block_m(int batch, int heads, int n_q) {
@@ -436,18 +673,32 @@ int sdpa_bf16_block_m(int batch, int heads, int n_q) {
 #define ATTN_SDPA_NS_LONG 4
 #endif
 
+#ifndef ATTN_SDPA_Q64
+#define ATTN_SDPA_Q64 0
+#endif
+
 hipError_t launch_sdpa_bf16(const SdpaBf16Params& p_in, hipStream_t stream) {
   SdpaBf16Params p = p_in;
   const int bm = sdpa_bf16_block_m(p.batch, p.heads, p.n_q);
   p.n_qblocks = (p.n_q + bm - 1) / bm;
   const int64_t grid = (int64_t)p.n_qblocks * p.batch * p.heads;
   if (grid == 0) return hipSuccess;
-  if (p.n_kv <= 64 * (ATTN_SDPA_NS_SHORT - 1) + 64)
+  const bool short_kv = p.n_kv <= 64 * ATTN_SDPA_NS_SHORT;
+#if ATTN_SDPA_Q64
+  if (short_kv)
+    hipLaunchKernelGGL((sdpa_fwd_bf16_d64_q64<ATTN_SDPA_NS_SHORT>), dim3((unsigned)grid), dim3(128), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((sdpa_fwd_bf16_d64_q64<ATTN_SDPA_NS_LONG>), dim3((unsigned)grid), dim3(128), 0,
+                       stream, p);
+#else
+  if (short_kv)
     hipLaunchKernelGGL((sdpa_fwd_bf16_d64<4, ATTN_SDPA_NS_SHORT>), dim3((unsigned)grid), dim3(256), 0,
                        stream, p);
   else
     hipLaunchKernelGGL((sdpa_fwd_bf16_d64<4, ATTN_SDPA_NS_LONG>), dim3((unsigned)grid), dim3(256), 0,
                        stream, p);
+#endif
   return hipGetLastError();
 }
 
