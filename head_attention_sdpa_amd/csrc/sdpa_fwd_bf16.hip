@@ -143,18 +143,25 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>(p);
 }
 
-template <int NW, int NS>
-__global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_d64(const SdpaBf16Params p) {
-  constexpr int BM = 32 * NW;            // queries per workgroup
-  constexpr int TILE_E = BN * D;         // bf16 elements per K or V tile (8 KiB)
-  constexpr int IPT = 16 / NW;           // DMA instructions per wave per stage (8 K + 8 V row blocks)
-  static_assert(IPT * NW == 16 && NS >= 3, "bad configuration");
-  static_assert(NW * 32 * D <= 2 * TILE_E, "the Q rows must fit in one ring stage");
-  __shared__ __attribute__((aligned(1024))) __bf16 smem[NS * 2 * TILE_E];  // [stage][K, V][64][64]
+// One workgroup = (batch, head, 32*NW queries); wave w owns queries
+// 32w..32w+31 of the block.  Per key tile the workgroup waits for its DMA,
+// meets at one barrier, refills the stage the previous tile used, and every
+// wave computes S^T, the masked online softmax and P.V for its queries.
+// There is no software pipeline inside a wave: the waves of a SIMD (WPE of
+// them, at most 512/WPE VGPRs each) interleave their vector and matrix work,
+// and the NS-stage ring is small enough that WPE workgroups share a CU's LDS.
+template <int NW, int NS, int WPE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void sdpa_fwd_bf16_d64(const SdpaBf16Params p) {
+  constexpr int BM = 32 * NW;
+  constexpr int TILE_E = BN * D;
+  constexpr int IPT = 16 / NW;
+  static_assert(IPT * NW == 16 && NS >= 2, "bad configuration");
+  __shared__ __attribute__((aligned(1024))) __bf16 smem[NS * 2 * TILE_E];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: DMA targets live in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i32 = lane & 31, g = lane >> 5;
 
   int bh, qb;
@@ -168,8 +175,6 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_d64(const SdpaBf16Param
   const int q0 = qb * BM;
   const int qw0 = q0 + wave * 32;
   const int qi = qw0 + i32;
-
-  // keys this workgroup / this wave needs (queries >= Lq are zeros: need nothing)
   int kv_end = Lkv, wkv_end = Lkv;
   if (p.causal) {
     kv_end = min(kv_end, min(q0 + BM, Lq));
@@ -182,22 +187,9 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_d64(const SdpaBf16Param
   const __bf16* Qb = reinterpret_cast<const __bf16*>(p.q) + b * p.qs_b + h * p.qs_h;
   const __bf16* Kb = reinterpret_cast<const __bf16*>(p.k) + b * p.ks_b + h * p.ks_h;
   const __bf16* Vb = reinterpret_cast<const __bf16*>(p.v) + b * p.vs_b + h * p.vs_h;
-
-  // Buffer descriptors over this (b, h)'s rows: each range ends with the last
-  // valid row, so loads of rows past the lengths return zeros (zero K/V keep
-  // 0 * V finite where the padding holds NaN; zero Q rows keep discarded
-  // columns finite).  Row strides are >= 64 elements (host-checked).
-  const uint32_t q_bytes = Lq > 0 ? (uint32_t)((int64_t)(Lq - 1) * p.qs_n * 2 + 128) : 0u;
   const uint32_t k_bytes = Lkv > 0 ? (uint32_t)((int64_t)(Lkv - 1) * p.ks_n * 2 + 128) : 0u;
   const uint32_t v_bytes = Lkv > 0 ? (uint32_t)((int64_t)(Lkv - 1) * p.vs_n * 2 + 128) : 0u;
-  const i32x4 rs_q = make_rsrc(Qb, q_bytes);
 
-  // DMA of key tile t into stage t % NS: instruction u of the tile covers row
-  // block u & 7 of K (u < 8) or V (u >= 8); lane l fills row 8*(u&7) + l/8 at
-  // chunk position l%8 with the global chunk that the swizzle maps there.
-  // Each lane's byte offset inside a tile is fixed; the tile advance moves
-  // the (scalar) descriptor base and shrinks its range, so the range check
-  // keeps zero-filling the rows past the key length.
   uint32_t dma_off[IPT];
 #pragma unroll
   for (int i = 0; i < IPT; ++i) {
@@ -220,98 +212,54 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_d64(const SdpaBf16Param
     }
   };
 
-  // Q: each wave copies its 32 query rows (4 KiB) into the last ring stage,
-  // which the prologue leaves free; the first in-loop refill of that stage
-  // comes after every wave has read its Q fragments (barrier at blk = 0).
-  const __bf16* Qs = smem + (NS - 1) * 2 * TILE_E + wave * 32 * D;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 8 * i + (lane >> 3);
-    const int chunk = (lane & 7) ^ swz_k(r);
-    const uint32_t voff = (uint32_t)(((int64_t)(qw0 + r) * p.qs_n + chunk * 8) * 2);
-    dma16(voff, rs_q, lds_addr(Qs + 8 * i * D));
-  }
-  int prologue = 0;
 #pragma unroll
   for (int t = 0; t < NS - 1; ++t)
-    if (t < nblk) {
-      issue_tile(t);
-      ++prologue;
-    }
-  // Q^T operand: lane holds query qi, d = 16*dstep + 8*g + 0..7
-  wait_vmcnt_le<IPT>(prologue * IPT);
+    if (t < nblk) issue_tile(t);
+  // Q^T operand straight from memory: lane holds query qi, d = 16*dstep + 8*g + 0..7
+  // (rows past the query length are zeros).  The empty asm consumes the
+  // registers, so the wait for these loads happens here, once, and not inside
+  // the loop.
   bf16x8 qf[4];
+  {
+    const __bf16* qrow = Qb + (int64_t)min(qi, max(Lq - 1, 0)) * p.qs_n + 8 * g;
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const int c = 2 * d + g;
-    qf[d] = *reinterpret_cast<const bf16x8*>(Qs + i32 * D + 8 * (c ^ swz_k(i32)));
+    for (int d = 0; d < 4; ++d) {
+      bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 16 * d);
+      qf[d] = qi < Lq ? v : bf16x8{};
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) asm volatile("" ::"v"(qf[d]));
   }
 
-  f32x16 o0 = {}, o1 = {};     // O^T for value columns 0..31 and 32..63
-  float m = -INFINITY;         // running max of scale*log2(e)*score
-  float l = 0.f;               // running sum (this lane's half of the keys)
+  f32x16 o0 = {}, o1 = {};
+  float m = -INFINITY;
+  float l = 0.f;
   const float c2 = p.scale_log2;
-
-  // transposed-read addressing inside a 16-lane group
   const int k16 = lane & 15;
   const int chalf = (lane >> 4) & 1;
   const int tr_row = g * 4 + (k16 >> 2);
-  const int tr_chunk = 2 * chalf + ((k16 & 3) >> 1);   // + 4*cb
-  const int tr_half = 4 * (k16 & 1);                   // element offset inside the chunk
+  const int tr_chunk = 2 * chalf + ((k16 & 3) >> 1);
+  const int tr_half = 4 * (k16 & 1);
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 
-  // S^T = K_tile . Q^T for the tile in `stage`: s0 keys 0..31, s1 keys 32..63
-  auto qk = [&](int stage, f32x16& s0, f32x16& s1) {
-    const __bf16* Ks = smem + stage * 2 * TILE_E;
-    s0 = f32x16{};
-    s1 = f32x16{};
+  for (int blk = 0; blk < nblk; ++blk) {
+    // tile blk has landed once at most min(NS-2, nblk-1-blk) newer tiles are in flight
+    wait_vmcnt_le<IPT>(min(NS - 2, nblk - 1 - blk) * IPT);
+    barrier_lds();  // tile blk visible; every wave is done with tile blk-1
+    if (blk + NS - 1 < nblk) issue_tile(blk + NS - 1);  // into the stage of tile blk-1
+    const int key0 = blk * BN;
+    if (key0 >= wkv_end) continue;  // wave-uniform: keys after this wave's queries
+    const __bf16* Ks = smem + (blk % NS) * 2 * TILE_E;
+    const __bf16* Vs = Ks + TILE_E;
+    f32x16 sc0 = {}, sc1 = {};
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const int c = 2 * d + g;
       const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + i32 * D + 8 * (c ^ swz_k(i32)));
       const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Ks + (32 + i32) * D + 8 * (c ^ swz_k(32 + i32)));
-      s0 = mfma32(ka, qf[d], s0);
-      s1 = mfma32(kb, qf[d], s1);
+      sc0 = mfma32(ka, qf[d], sc0);
+      sc1 = mfma32(kb, qf[d], sc1);
     }
-  };
-
-  // One iteration of the software pipeline.  The softmax and P.V of tile blk
-  // run in four blocks of 16 keys; between them the wave issues one d-step
-  // (two MFMAs) of the Q.K^T products of tile blk+1 (into sn) and the two
-  // P.V MFMAs of the block just computed.  Every MFMA is thus separated from
-  // the one it depends on by a block of vector work, so the matrix cores run
-  // the next tile's scores and this tile's P.V while the vector ALUs run the
-  // softmax.  The loop below is unrolled by two with the score buffers
-  // swapping roles, so no registers are copied between iterations.
-  auto step = [&](int blk, f32x16& sc0, f32x16& sc1, f32x16& sn0, f32x16& sn1) {
-    const int key0 = blk * BN;
-    bool do_next = false;
-    if (blk + 1 < nblk) {
-      // tile blk+1 has landed once at most min(NS-3, nblk-2-blk) newer tiles are in flight
-      wait_vmcnt_le<IPT>(min(NS - 3, nblk - 2 - blk) * IPT);
-      barrier_lds();  // tile blk+1 visible; every wave is past P.V of tile blk-1
-      if (blk + NS - 1 < nblk) issue_tile(blk + NS - 1);  // into the stage of tile blk-1
-      do_next = key0 + BN < wkv_end;
-    }
-    const __bf16* Kn = smem + ((blk + 1) % NS) * 2 * TILE_E;
-    // one d-step of S^T(next) = K_next . Q^T
-    auto qk_step = [&](int d) {
-      const int c = 2 * d + g;
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Kn + i32 * D + 8 * (c ^ swz_k(i32)));
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Kn + (32 + i32) * D + 8 * (c ^ swz_k(32 + i32)));
-      sn0 = mfma32(ka, qf[d], d == 0 ? f32x16{} : sn0);
-      sn1 = mfma32(kb, qf[d], d == 0 ? f32x16{} : sn1);
-    };
-    if (key0 >= wkv_end) {  // wave-uniform: tile entirely after this wave's queries
-      if (do_next)
-#pragma unroll
-        for (int d = 0; d < 4; ++d) qk_step(d);
-      return;
-    }
-    const __bf16* Vs = smem + (blk % NS) * 2 * TILE_E + TILE_E;
-
-    // -inf for illegal keys (only tiles that cross the length or the
-    // diagonal): key key0 + pos is legal iff pos <= thr, where the lane's
-    // register r holds pos = 8*(r/4) + 4*g + r%4 (+32 in sc1)
     if (key0 + BN > Lkv || (p.causal && key0 + BN - 1 > qw0)) {
       const int lim = p.causal ? min(Lkv - 1, qi) : Lkv - 1;
       const int thr = lim - key0 - 4 * g;
@@ -322,20 +270,14 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_d64(const SdpaBf16Param
         if (pos + 32 > thr) sc1[r] = -INFINITY;
       }
     }
-
-    // online softmax.  A lane's running max m is only moved (and its O, l
-    // rescaled) when its tile max exceeds m by more than 8 (log2 units):
-    // otherwise the stale m stays the shift, which the softmax is invariant
-    // to, and the weights stay below 2^8.  The decision is per lane, so a
-    // query's arithmetic never depends on the other queries of the wave.
     float mx = fmaxf(sc0[0], sc1[0]);
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, sc0[r]), sc1[r]);
     mx = max_with_partner(mx) * c2;
     const bool grow = mx > m + 8.f;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform skip; per-lane decision
-      const float m_new = grow ? mx : m;     // lanes that do not grow keep m: alpha = 1 exactly
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // m = -inf: alpha = 0
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? mx : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
       l *= alpha;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -344,20 +286,13 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_d64(const SdpaBf16Param
       }
       m = m_new;
     }
-    const float m_use = (m == -INFINITY) ? 0.f : m;  // no legal key yet: avoid -inf - -inf
-
-    // Blocks (jb, s) cover keys 32*jb + 16*s + 0..15.  The P^T operand's
-    // element t is key 32*jb + 16*s + 8*(t/4) + 4*g + t%4 (the C layout of
-    // the scores); the row sum adds the bf16-rounded weights (the ones P.V
-    // uses), two per instruction with a dot product against (1, 1).  The V^T
-    // operand for (cb, jb, s) is V[key(t)][32*cb + lane%32], read transposed.
-    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+    const float m_use = (m == -INFINITY) ? 0.f : m;
     float rs = 0.f;
 #pragma unroll
     for (int blkq = 0; blkq < 4; ++blkq) {
       const int jb = blkq >> 1, s = blkq & 1;
       const f32x16& sc = jb ? sc1 : sc0;
-      bf16x4 part[2][2];  // [cb][lo/hi rows]
+      bf16x4 part[2][2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int row = 32 * jb + 16 * s + 8 * hh + tr_row;
@@ -374,7 +309,6 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_d64(const SdpaBf16Param
         pp[t] = __builtin_convertvector(e, bf16x2);
         rs = __builtin_amdgcn_fdot2_f32_bf16(pp[t], ones, rs, false);
       }
-      if (do_next) qk_step(blkq);
       const bf16x8 pf = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
                                                 __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
                                                 0, 1, 2, 3, 4, 5, 6, 7);
@@ -384,21 +318,8 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_d64(const SdpaBf16Param
       o1 = mfma32(va1, pf, o1);
     }
     l += rs;
-  };
-
-  f32x16 sa0 = {}, sa1 = {}, sb0 = {}, sb1 = {};
-  if (nblk > 0) {
-    wait_vmcnt_le<IPT>(min(NS - 2, nblk - 1) * IPT);   // tile 0 landed
-    barrier_lds();
-    if (0 < wkv_end) qk(0, sa0, sa1);
-  }
-  for (int blk = 0; blk < nblk; blk += 2) {
-    step(blk, sa0, sa1, sb0, sb1);
-    if (blk + 1 < nblk) step(blk + 1, sb0, sb1, sa0, sa1);
   }
 
-  // epilogue: O = O^T / l, rounded once to bf16; rows without a legal key or
-  // beyond the query length are zeros.
   const float lt = sum_with_partner(l);
   if (qi < p.n_q) {
     const bool valid = (qi < Lq) && (lt > 0.f);
@@ -420,240 +341,6 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_bf16_d64(const SdpaBf16Param
   }
 }
 
-// ---------------------------------------------------------------------------
-// Variant with 64 queries per wave (two 32-query column blocks): every K and
-// V fragment read from LDS feeds two MFMAs, which halves the LDS read traffic
-// per MFMA (the transposed V reads are the most expensive LDS operation).
-// Two waves per workgroup (128 queries), same grid as the 32-query kernel.
-// Within a tile the softmax of one query block overlaps the MFMAs of the
-// other: Q.K^T of block 0, Q.K^T of block 1, softmax 0, P.V 0, softmax 1, P.V 1.
-template <int NS>
-__global__ __launch_bounds__(128) void sdpa_fwd_bf16_d64_q64(const SdpaBf16Params p) {
-  constexpr int NW = 2, QB = 2;
-  constexpr int BM = 32 * QB * NW;       // 128 queries per workgroup
-  constexpr int TILE_E = BN * D;
-  constexpr int IPT = 16 / NW;           // 8 DMA instructions per wave per stage
-  static_assert(NS >= 2, "bad configuration");
-  static_assert(NW * QB * 32 * D <= 2 * TILE_E, "the Q rows must fit in one ring stage");
-  __shared__ __attribute__((aligned(1024))) __bf16 smem[NS * 2 * TILE_E];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int i32 = lane & 31, g = lane >> 5;
-
-  int bh, qb;
-  map_block(blockIdx.x, p.batch * p.heads, p.n_qblocks, p.causal, bh, qb);
-  const int b = bh / p.heads, h = bh - b * p.heads;
-
-  int Lq = p.n_q, Lkv = p.n_kv;
-  if (p.seqlens_q) Lq = min(max(p.seqlens_q[b], 0), p.n_q);
-  if (p.seqlens_kv) Lkv = min(max(p.seqlens_kv[b], 0), p.n_kv);
-
-  const int q0 = qb * BM;
-  const int qw0 = q0 + wave * 64;         // this wave's 64 queries: qw0 .. qw0+63
-  int qi[QB];
-#pragma unroll
-  for (int c = 0; c < QB; ++c) qi[c] = qw0 + 32 * c + i32;
-
-  int kv_end = Lkv, wkv_end = Lkv;
-  if (p.causal) {
-    kv_end = min(kv_end, min(q0 + BM, Lq));
-    wkv_end = min(wkv_end, min(qw0 + 64, Lq));
-  }
-  if (q0 >= Lq) kv_end = 0;
-  if (qw0 >= Lq) wkv_end = 0;
-  const int nblk = (kv_end + BN - 1) / BN;
-
-  const __bf16* Qb = reinterpret_cast<const __bf16*>(p.q) + b * p.qs_b + h * p.qs_h;
-  const __bf16* Kb = reinterpret_cast<const __bf16*>(p.k) + b * p.ks_b + h * p.ks_h;
-  const __bf16* Vb = reinterpret_cast<const __bf16*>(p.v) + b * p.vs_b + h * p.vs_h;
-  const uint32_t q_bytes = Lq > 0 ? (uint32_t)((int64_t)(Lq - 1) * p.qs_n * 2 + 128) : 0u;
-  const uint32_t k_bytes = Lkv > 0 ? (uint32_t)((int64_t)(Lkv - 1) * p.ks_n * 2 + 128) : 0u;
-  const uint32_t v_bytes = Lkv > 0 ? (uint32_t)((int64_t)(Lkv - 1) * p.vs_n * 2 + 128) : 0u;
-  const i32x4 rs_q = make_rsrc(Qb, q_bytes);
-
-  uint32_t dma_off[IPT];
-#pragma unroll
-  for (int i = 0; i < IPT; ++i) {
-    const int u = wave * IPT + i;
-    const bool is_v = u >= 8;
-    const int r = 8 * (u & 7) + (lane >> 3);
-    const int chunk = (lane & 7) ^ (is_v ? swz_v(r) : swz_k(r));
-    dma_off[i] = (uint32_t)(((int64_t)r * (is_v ? p.vs_n : p.ks_n) + chunk * 8) * 2);
-  }
-  auto issue_tile = [&](int t) {
-    const int64_t k_adv = (int64_t)t * BN * p.ks_n, v_adv = (int64_t)t * BN * p.vs_n;
-    const i32x4 rk = make_rsrc(Kb + k_adv, (uint32_t)max<int64_t>(0, (int64_t)k_bytes - 2 * k_adv));
-    const i32x4 rv = make_rsrc(Vb + v_adv, (uint32_t)max<int64_t>(0, (int64_t)v_bytes - 2 * v_adv));
-#pragma unroll
-    for (int i = 0; i < IPT; ++i) {
-      const int u = wave * IPT + i;
-      if (u < 8) dma16(dma_off[i], rk, lds_addr(smem + (t % NS) * 2 * TILE_E + u * 512));
-      else dma16(dma_off[i], rv, lds_addr(smem + (t % NS) * 2 * TILE_E + TILE_E + (u - 8) * 512));
-    }
-  };
-
-  // Q: each wave copies its 64 query rows (8 KiB) into the last ring stage
-  const __bf16* Qs = smem + (NS - 1) * 2 * TILE_E + wave * 64 * D;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 8 * i + (lane >> 3);
-    const int chunk = (lane & 7) ^ swz_k(r);
-    const uint32_t voff = (uint32_t)(((int64_t)(qw0 + r) * p.qs_n + chunk * 8) * 2);
-    dma16(voff, rs_q, lds_addr(Qs + 8 * i * D));
-  }
-  int prologue = 0;
-#pragma unroll
-  for (int t = 0; t < NS - 1; ++t)
-    if (t < nblk) {
-      issue_tile(t);
-      ++prologue;
-    }
-  wait_vmcnt_le<IPT>(prologue * IPT);
-  bf16x8 qf[QB][4];
-#pragma unroll
-  for (int c = 0; c < QB; ++c)
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const int r = 32 * c + i32, ch = 2 * d + g;
-      qf[c][d] = *reinterpret_cast<const bf16x8*>(Qs + r * D + 8 * (ch ^ swz_k(r)));
-    }
-
-  f32x16 o[QB][2] = {};       // O^T[query block][value columns 0..31 / 32..63]
-  float m[QB], l[QB];
-#pragma unroll
-  for (int c = 0; c < QB; ++c) {
-    m[c] = -INFINITY;
-    l[c] = 0.f;
-  }
-  const float c2 = p.scale_log2;
-  const int k16 = lane & 15;
-  const int chalf = (lane >> 4) & 1;
-  const int tr_row = g * 4 + (k16 >> 2);
-  const int tr_chunk = 2 * chalf + ((k16 & 3) >> 1);
-  const int tr_half = 4 * (k16 & 1);
-  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-
-  for (int blk = 0; blk < nblk; ++blk) {
-    wait_vmcnt_le<IPT>(min(NS - 2, nblk - 1 - blk) * IPT);   // tile blk landed
-    barrier_lds();                                           // stage (blk-1)%NS free
-    if (blk + NS - 1 < nblk) issue_tile(blk + NS - 1);
-    const int key0 = blk * BN;
-    if (key0 >= wkv_end) continue;  // wave-uniform
-    const __bf16* Ks = smem + (blk % NS) * 2 * TILE_E;
-    const __bf16* Vs = Ks + TILE_E;
-
-    // S^T[query block c][key half kb] = K_kb . Q_c^T ; each K fragment feeds both query blocks
-    f32x16 sc[QB][2];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const int ch = 2 * d + g;
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + i32 * D + 8 * (ch ^ swz_k(i32)));
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Ks + (32 + i32) * D + 8 * (ch ^ swz_k(32 + i32)));
-#pragma unroll
-      for (int c = 0; c < QB; ++c) {
-        sc[c][0] = mfma32(ka, qf[c][d], d == 0 ? f32x16{} : sc[c][0]);
-        sc[c][1] = mfma32(kb, qf[c][d], d == 0 ? f32x16{} : sc[c][1]);
-      }
-    }
-
-    // softmax of each query block, then P.V with V fragments shared by both blocks
-    bf16x8 pf[QB][4];   // [query block][key block (jb, s) = 2*jb + s]
-#pragma unroll
-    for (int c = 0; c < QB; ++c) {
-      if (key0 + BN > Lkv || (p.causal && key0 + BN - 1 > qw0 + 32 * c)) {
-        const int lim = p.causal ? min(Lkv - 1, qi[c]) : Lkv - 1;
-        const int thr = lim - key0 - 4 * g;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int pos = 8 * (r >> 2) + (r & 3);
-          if (pos > thr) sc[c][0][r] = -INFINITY;
-          if (pos + 32 > thr) sc[c][1][r] = -INFINITY;
-        }
-      }
-      float mx = fmaxf(sc[c][0][0], sc[c][1][0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, sc[c][0][r]), sc[c][1][r]);
-      mx = max_with_partner(mx) * c2;
-      const bool grow = mx > m[c] + 8.f;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float m_new = grow ? mx : m[c];
-        const float alpha = __builtin_amdgcn_exp2f(m[c] - m_new);
-        l[c] *= alpha;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          o[c][0][r] *= alpha;
-          o[c][1][r] *= alpha;
-        }
-        m[c] = m_new;
-      }
-      const float m_use = (m[c] == -INFINITY) ? 0.f : m[c];
-      float rs = 0.f;
-#pragma unroll
-      for (int kbk = 0; kbk < 4; ++kbk) {
-        const int jb = kbk >> 1, s = kbk & 1;
-        bf16x2 pp[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const f32x2 e = {__builtin_amdgcn_exp2f(fmaf(sc[c][jb][8 * s + 2 * t], c2, -m_use)),
-                           __builtin_amdgcn_exp2f(fmaf(sc[c][jb][8 * s + 2 * t + 1], c2, -m_use))};
-          pp[t] = __builtin_convertvector(e, bf16x2);
-          rs = __builtin_amdgcn_fdot2_f32_bf16(pp[t], ones, rs, false);
-        }
-        pf[c][kbk] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
-                                             __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
-                                             0, 1, 2, 3, 4, 5, 6, 7);
-      }
-      l[c] += rs;
-    }
-#pragma unroll
-    for (int kbk = 0; kbk < 4; ++kbk) {
-      const int jb = kbk >> 1, s = kbk & 1;
-      bf16x4 part[2][2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int row = 32 * jb + 16 * s + 8 * hh + tr_row;
-        const __bf16* vrow = Vs + row * D + tr_half;
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-          part[cb][hh] = tr_read(vrow + 8 * ((4 * cb + tr_chunk) ^ swz_v(row)));
-      }
-      const bf16x8 va0 = __builtin_shufflevector(part[0][0], part[0][1], 0, 1, 2, 3, 4, 5, 6, 7);
-      const bf16x8 va1 = __builtin_shufflevector(part[1][0], part[1][1], 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-      for (int c = 0; c < QB; ++c) {
-        o[c][0] = mfma32(va0, pf[c][kbk], o[c][0]);
-        o[c][1] = mfma32(va1, pf[c][kbk], o[c][1]);
-      }
-    }
-  }
-
-  // epilogue per query block
-#pragma unroll
-  for (int c = 0; c < QB; ++c) {
-    const float lt = sum_with_partner(l[c]);
-    if (qi[c] < p.n_q) {
-      const bool valid = (qi[c] < Lq) && (lt > 0.f);
-      const float inv = valid ? 1.f / lt : 0.f;
-      __bf16* orow = reinterpret_cast<__bf16*>(p.o) + b * p.os_b + h * p.os_h + (int64_t)qi[c] * p.os_n;
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        bf16x4 w0, w1;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          w0[t] = (__bf16)(o[c][0][4 * rg + t] * inv);
-          w1[t] = (__bf16)(o[c][1][4 * rg + t] * inv);
-        }
-        *reinterpret_cast<u32x2*>(orow + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, w0);
-        *reinterpret_cast<u32x2*>(orow + 32 + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, w1);
-      }
-      if (p.lse && g == 0)
-        p.lse[((int64_t)b * p.heads + h) * p.n_q + qi[c]] = valid ? (m[c] + __log2f(lt)) * LN2 : -INFINITY;
-    }
-  }
-}
-
 }  // namespace
 
 int sdpa_bf16_block_m(int batch, int heads, int n_q) {
@@ -663,42 +350,19 @@ int sdpa_bf16_block_m(int batch, int heads, int n_q) {
   return 128;
 }
 
-// Ring depth: with up to 5 key tiles (n_kv <= 320) a 5-stage ring puts every
-// tile of the workgroup in flight at once (one memory round trip); longer
-// sequences use 4 stages (64 KiB, two workgroups per CU).
-#ifndef ATTN_SDPA_NS_SHORT
-#define ATTN_SDPA_NS_SHORT 5
-#endif
-#ifndef ATTN_SDPA_NS_LONG
-#define ATTN_SDPA_NS_LONG 4
-#endif
-
-#ifndef ATTN_SDPA_Q64
-#define ATTN_SDPA_Q64 0
-#endif
+// Four waves of 32 queries, a two-stage ring (32 KiB of LDS) and at most 128
+// VGPRs: four workgroups (16 waves) per CU, for every sequence length.
+constexpr int kWaves = 4, kStages = 2, kWavesPerSimd = 4;
 
 hipError_t launch_sdpa_bf16(const SdpaBf16Params& p_in, hipStream_t stream) {
   SdpaBf16Params p = p_in;
   const int bm = sdpa_bf16_block_m(p.batch, p.heads, p.n_q);
+  static_assert(32 * kWaves == 128, "block size and kernel disagree");
   p.n_qblocks = (p.n_q + bm - 1) / bm;
   const int64_t grid = (int64_t)p.n_qblocks * p.batch * p.heads;
   if (grid == 0) return hipSuccess;
-  const bool short_kv = p.n_kv <= 64 * ATTN_SDPA_NS_SHORT;
-#if ATTN_SDPA_Q64
-  if (short_kv)
-    hipLaunchKernelGGL((sdpa_fwd_bf16_d64_q64<ATTN_SDPA_NS_SHORT>), dim3((unsigned)grid), dim3(128), 0,
-                       stream, p);
-  else
-    hipLaunchKernelGGL((sdpa_fwd_bf16_d64_q64<ATTN_SDPA_NS_LONG>), dim3((unsigned)grid), dim3(128), 0,
-                       stream, p);
-#else
-  if (short_kv)
-    hipLaunchKernelGGL((sdpa_fwd_bf16_d64<4, ATTN_SDPA_NS_SHORT>), dim3((unsigned)grid), dim3(256), 0,
-                       stream, p);
-  else
-    hipLaunchKernelGGL((sdpa_fwd_bf16_d64<4, ATTN_SDPA_NS_LONG>), dim3((unsigned)grid), dim3(256), 0,
-                       stream, p);
-#endif
+  hipLaunchKernelGGL((sdpa_fwd_bf16_d64<kWaves, kStages, kWavesPerSimd>), dim3((unsigned)grid),
+                     dim3(64 * kWaves), 0, stream, p);
   return hipGetLastError();
 }
 
