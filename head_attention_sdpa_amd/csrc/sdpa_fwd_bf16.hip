@@ -156,7 +156,8 @@ void sdpa_fwd_bf16_d64(const SdpaBf16Params p) {
   constexpr int BM = 32 * NW;
   constexpr int TILE_E = BN * D;
   constexpr int IPT = 16 / NW;
-  static_assert(IPT * NW == 16 && NS >= 2, "bad configuration");
+  static_assert(IPT * NW == 16 && NS >= 2 && NS <= 6, "bad configuration");
+  static_assert(NW * 32 * D <= 2 * TILE_E, "the Q rows must fit in one ring stage");
   __shared__ __attribute__((aligned(1024))) __bf16 smem[NS * 2 * TILE_E];
 
   const int tid = threadIdx.x;
@@ -187,8 +188,11 @@ void sdpa_fwd_bf16_d64(const SdpaBf16Params p) {
   const __bf16* Qb = reinterpret_cast<const __bf16*>(p.q) + b * p.qs_b + h * p.qs_h;
   const __bf16* Kb = reinterpret_cast<const __bf16*>(p.k) + b * p.ks_b + h * p.ks_h;
   const __bf16* Vb = reinterpret_cast<const __bf16*>(p.v) + b * p.vs_b + h * p.vs_h;
+  const uint32_t q_bytes = Lq > 0 ? (uint32_t)((int64_t)(Lq - 1) * p.qs_n * 2 + 128) : 0u;
   const uint32_t k_bytes = Lkv > 0 ? (uint32_t)((int64_t)(Lkv - 1) * p.ks_n * 2 + 128) : 0u;
   const uint32_t v_bytes = Lkv > 0 ? (uint32_t)((int64_t)(Lkv - 1) * p.vs_n * 2 + 128) : 0u;
+
+  const i32x4 rs_q = make_rsrc(Qb, q_bytes);
 
   uint32_t dma_off[IPT];
 #pragma unroll
@@ -212,23 +216,33 @@ void sdpa_fwd_bf16_d64(const SdpaBf16Params p) {
     }
   };
 
+  // Q: each wave copies its 32 query rows (4 KiB) into the last ring stage,
+  // which the prologue leaves free; the first refill of that stage is issued
+  // after the barrier of the first iteration, when every wave has read its Q
+  // fragments.  Q goes first, so once at most (prologue tiles) DMAs are in
+  // flight Q has landed, while the prologue tiles may still be on their way.
+  const __bf16* Qs = smem + (NS - 1) * 2 * TILE_E + wave * 32 * D;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * i + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz_k(r);
+    const uint32_t voff = (uint32_t)(((int64_t)(qw0 + r) * p.qs_n + chunk * 8) * 2);
+    dma16(voff, rs_q, lds_addr(Qs + 8 * i * D));
+  }
+  int prologue = 0;
 #pragma unroll
   for (int t = 0; t < NS - 1; ++t)
-    if (t < nblk) issue_tile(t);
-  // Q^T operand straight from memory: lane holds query qi, d = 16*dstep + 8*g + 0..7
-  // (rows past the query length are zeros).  The empty asm consumes the
-  // registers, so the wait for these loads happens here, once, and not inside
-  // the loop.
-  bf16x8 qf[4];
-  {
-    const __bf16* qrow = Qb + (int64_t)min(qi, max(Lq - 1, 0)) * p.qs_n + 8 * g;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + 16 * d);
-      qf[d] = qi < Lq ? v : bf16x8{};
+    if (t < nblk) {
+      issue_tile(t);
+      ++prologue;
     }
+  wait_vmcnt_le<IPT>(prologue * IPT);
+  // Q^T operand: lane holds query qi, d = 16*dstep + 8*g + 0..7
+  bf16x8 qf[4];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) asm volatile("" ::"v"(qf[d]));
+  for (int d = 0; d < 4; ++d) {
+    const int c = 2 * d + g;
+    qf[d] = *reinterpret_cast<const bf16x8*>(Qs + i32 * D + 8 * (c ^ swz_k(i32)));
   }
 
   f32x16 o0 = {}, o1 = {};
@@ -351,7 +365,9 @@ int sdpa_bf16_block_m(int batch, int heads, int n_q) {
 }
 
 // Four waves of 32 queries, a two-stage ring (32 KiB of LDS) and at most 128
-// VGPRs: four workgroups (16 waves) per CU, for every sequence length.
+// VGPRs: four workgroups (16 waves) per CU.  Measured on MI355X, this beats
+// deeper rings (3-5 stages, fewer waves per SIMD) at every sequence length,
+// the 256-key decoder included.
 constexpr int kWaves = 4, kStages = 2, kWavesPerSimd = 4;
 
 hipError_t launch_sdpa_bf16(const SdpaBf16Params& p_in, hipStream_t stream) {
