@@ -173,16 +173,18 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(const GemmBf16Params p) {
 }
 
 // ---------------------------------------------------------------------------
-// Main kernel for the common shapes (column panels a multiple of 128 wide,
-// K a multiple of 64): workgroup tile 256 (m) x 128 (n) x 64 (k), four waves
-// in a 2 x 2 arrangement of 128 (m) x 64 (n) wave tiles (8 MFMA accumulators
-// per wave: 8 MFMAs per 4 + 4 LDS reads).  X and W tiles are copied global ->
-// LDS by buffer_load ... lds into a 3-stage ring; rows past M read as zeros
-// from the buffer range.  LDS layouts are XOR-swizzled (no padding):
-//   X tile [256 m][64 k]: 16-byte chunk c of row r at position c ^ ((r>>1)&7)
-//     (16 consecutive rows read one chunk each: distinct banks)
-//   W tile [64 k][128 n]: chunk c of row r at position c ^ (4*(r&3))
-//     (transposed reads touch 4 consecutive rows x 2 or 4 chunks)
+// Main kernel for the common shapes (column panels a multiple of 256 wide, K
+// a multiple of 32): workgroup tile 256 (m) x 256 (n), eight waves (two per
+// SIMD) in a 2 x 4 arrangement of 128 (m) x 64 (n) wave tiles (8 MFMA
+// accumulators per wave: 8 MFMAs per 4 + 4 LDS reads).  K advances 32 at a
+// time: the X and W slices of one step (16 KiB each) are copied global -> LDS
+// by buffer_load ... lds into an S-stage ring, so S-1 steps are in flight
+// while one is computed; rows past M read as zeros from the buffer range.
+// LDS layouts are XOR-swizzled (no padding):
+//   X slice [256 m][32 k], 64-byte rows: 16-byte chunk c of row r at position
+//     c ^ ((r>>2)&3) (16 consecutive rows read one chunk each: distinct banks)
+//   W slice, two halves of [32 k][128 n]: chunk c of row r at position
+//     c ^ (4*(r&3)) (transposed reads touch 4 consecutive rows x 2 or 4 chunks)
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
@@ -200,6 +202,15 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// wait until at most n (a multiple of Step, n <= 4*Step) DMA instructions are in flight
+template <int Step>
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  if (n <= 0) wait_vmcnt<0>();
+  else if (n <= Step) wait_vmcnt<Step>();
+  else if (n <= 2 * Step) wait_vmcnt<2 * Step>();
+  else if (n <= 3 * Step) wait_vmcnt<3 * Step>();
+  else wait_vmcnt<4 * Step>();
+}
 __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -207,23 +218,30 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>(p);
 }
 
-constexpr int M2 = 256, N2 = 128, K2 = 64, S2 = 3;
-constexpr int X_TILE = M2 * K2;          // bf16 elements (32 KiB)
-constexpr int W_TILE = K2 * N2;          // 16 KiB
-constexpr int STAGE2 = X_TILE + W_TILE;
-constexpr int IPW = (X_TILE + W_TILE) * 2 / 1024 / 4;  // DMA instructions per wave per stage (12)
+constexpr int M2 = 256, N2 = 256, K2 = 32;
+constexpr int X_SLICE = M2 * K2;         // bf16 elements (16 KiB)
+constexpr int W_HALF = K2 * 128;         // one [32 k][128 n] half of the W slice (8 KiB)
+constexpr int STAGE = X_SLICE + 2 * W_HALF;
+constexpr int NWAVES = 8;
+constexpr int IPW = STAGE * 2 / 1024 / NWAVES;   // 1 KiB DMA instructions per wave per stage (4)
 
-__device__ __forceinline__ int swz_x(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz_x(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int swz_w(int r) { return 4 * (r & 3); }
 
-__global__ __launch_bounds__(256) void gemm_bf16_dma_kernel(const GemmBf16Params p) {
-  __shared__ __attribute__((aligned(1024))) __bf16 smem[S2 * STAGE2];
+template <int S, bool BT>
+__global__ __launch_bounds__(64 * NWAVES) void gemm_bf16_dma_kernel(const GemmBf16Params p) {
+  static_assert(S >= 2 && S <= 5, "bad configuration");
+  __shared__ __attribute__((aligned(1024))) __bf16 smem[S * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int wm = wave & 1, wn = wave >> 1;   // wave tile: rows 128*wm.., cols 64*wn..
 
+  // Tile order: each XCD (workgroups are dealt to the 8 XCDs round-robin)
+  // gets a contiguous range of tiles, walked in groups of GM row tiles x all
+  // column tiles, so the workgroups running together on one XCD share X rows
+  // and W columns in its L2.
   constexpr int GM = 8;
   const int tiles_m = (p.M + M2 - 1) / M2;
   const int tiles_n = p.N / N2;
@@ -243,35 +261,48 @@ __global__ __launch_bounds__(256) void gemm_bf16_dma_kernel(const GemmBf16Params
   const int panel = n0 / p.n_panel;
   // (explicit selection keeps the kernel-argument array in scalar registers)
   const uint16_t* wpanel = panel == 0 ? p.b[0] : (panel == 1 ? p.b[1] : p.b[2]);
-  const __bf16* Wb = reinterpret_cast<const __bf16*>(wpanel) + (n0 - panel * p.n_panel);
-  const uint32_t w_bytes = (uint32_t)((int64_t)(p.K - 1) * p.n_panel * 2 + N2 * 2);
+  // BT: the panel is W^T, [n_panel][K]; the tile's 256 rows start at n0
+  const __bf16* Wb = reinterpret_cast<const __bf16*>(wpanel) +
+                     (BT ? (int64_t)(n0 - panel * p.n_panel) * p.K : (int64_t)(n0 - panel * p.n_panel));
+  const uint32_t w_bytes = BT ? (uint32_t)((int64_t)(N2 - 1) * p.K * 2 + (int64_t)p.K * 2)
+                              : (uint32_t)((int64_t)(p.K - 1) * p.n_panel * 2 + N2 * 2);
 
-  // per-lane DMA offsets (relative to the k-tile base)
+  // per-lane DMA offsets (relative to the k-step base).  Instruction u of a
+  // stage: u < 16 copies X rows 16u..16u+15 (four 16-byte chunks each);
+  // otherwise w = u - 16 copies rows 4*(w%8).. of W half w/8 (columns
+  // 128*(w/8)..).
   uint32_t off[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
-    const int u = wave * IPW + i;        // 0..31 X row blocks (8 rows), 32..47 W row blocks (4 rows)
-    if (u < 32) {
-      const int r = 8 * u + (lane >> 3);
-      const int c = (lane & 7) ^ swz_x(r);
+    const int u = wave * IPW + i;
+    if (u < 16) {
+      const int r = 16 * u + (lane >> 2);
+      const int c = (lane & 3) ^ swz_x(r);
       off[i] = (uint32_t)(((int64_t)r * p.lda + c * 8) * 2);
+    } else if (BT) {   // W^T rows 16w..16w+15 (n), four 16-byte chunks of k each
+      const int r = 16 * (u - 16) + (lane >> 2);
+      const int c = (lane & 3) ^ swz_x(r);
+      off[i] = (uint32_t)(((int64_t)r * p.K + c * 8) * 2);
     } else {
-      const int r = 4 * (u - 32) + (lane >> 4);
+      const int w = u - 16, half = w >> 3;
+      const int r = 4 * (w & 7) + (lane >> 4);
       const int c = (lane & 15) ^ swz_w(r);
-      off[i] = (uint32_t)(((int64_t)r * p.n_panel + c * 8) * 2);
+      off[i] = (uint32_t)(((int64_t)r * p.n_panel + 128 * half + c * 8) * 2);
     }
   }
   const int nk = p.K / K2;
   auto issue = [&](int kt) {
     const i32x4 rx = make_rsrc(Xb + kt * K2, x_bytes > (uint32_t)(kt * K2 * 2) ? x_bytes - kt * K2 * 2 : 0u);
-    const i32x4 rw = make_rsrc(Wb + (int64_t)kt * K2 * p.n_panel,
-                               (uint32_t)((int64_t)w_bytes - (int64_t)kt * K2 * p.n_panel * 2));
-    __bf16* st = smem + (kt % S2) * STAGE2;
+    const int64_t w_adv = BT ? (int64_t)kt * K2 : (int64_t)kt * K2 * p.n_panel;
+    const i32x4 rw = make_rsrc(Wb + w_adv, (uint32_t)((int64_t)w_bytes - w_adv * 2));
+    __bf16* st = smem + (kt % S) * STAGE;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int u = wave * IPW + i;   // wave-uniform: selects, no branches
-      const bool x = u < 32;
-      dma16(off[i], x ? rx : rw, lds_addr(st + (x ? u * 512 : X_TILE + (u - 32) * 512)));
+      const bool x = u < 16;
+      const int w = u - 16;
+      dma16(off[i], x ? rx : rw,
+            lds_addr(st + (x ? u * 512 : X_SLICE + (BT ? w * 512 : (w >> 3) * W_HALF + (w & 7) * 512))));
     }
   };
 
@@ -279,14 +310,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_dma_kernel(const GemmBf16Params
 
   const int k16 = lane & 15, chalf = (lane >> 4) & 1;
   const int tr_row = g * 8 + (k16 >> 2);           // + 16*ks (+4 for the second half)
-  const int tr_chunk = 2 * chalf + ((k16 & 3) >> 1);  // + 4*nb + 8*wn
+  const int tr_chunk = 2 * chalf + ((k16 & 3) >> 1);  // + 4*nb + 8*(wn&1)
   const int tr_half = 4 * (k16 & 1);
 
   // fragments of one 16-wide k-step: X rows (MFMA B operand) and W^T rows
-  // (MFMA A operand, transposed reads of the row-major W tile)
+  // (MFMA A operand, transposed reads of the row-major W slice)
   auto load_frags = [&](int kt, int ks, bf16x8 (&xf)[4], bf16x8 (&wf)[2]) {
-    const __bf16* Xs = smem + (kt % S2) * STAGE2;
-    const __bf16* Ws = Xs + X_TILE;
+    const __bf16* Xs = smem + (kt % S) * STAGE;
+    const __bf16* Ws = Xs + X_SLICE + (BT ? 0 : (wn >> 1) * W_HALF);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int r = wm * 128 + mb * 32 + l32;
@@ -295,29 +326,32 @@ __global__ __launch_bounds__(256) void gemm_bf16_dma_kernel(const GemmBf16Params
     }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const int c = 8 * wn + 4 * nb + tr_chunk;
-      const int r0 = 16 * ks + tr_row, r1 = r0 + 4;
-      const bf16x4 lo = tr_read(Ws + r0 * N2 + 8 * (c ^ swz_w(r0)) + tr_half);
-      const bf16x4 hi = tr_read(Ws + r1 * N2 + 8 * (c ^ swz_w(r1)) + tr_half);
-      wf[nb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      if (BT) {   // W^T slice [256 n][32 k], same layout as X
+        const int r = 64 * wn + 32 * nb + l32;
+        const int c = 2 * ks + g;
+        wf[nb] = *reinterpret_cast<const bf16x8*>(Ws + r * K2 + 8 * (c ^ swz_x(r)));
+      } else {
+        const int c = 8 * (wn & 1) + 4 * nb + tr_chunk;
+        const int r0 = 16 * ks + tr_row, r1 = r0 + 4;
+        const bf16x4 lo = tr_read(Ws + r0 * 128 + 8 * (c ^ swz_w(r0)) + tr_half);
+        const bf16x4 hi = tr_read(Ws + r1 * 128 + 8 * (c ^ swz_w(r1)) + tr_half);
+        wf[nb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
     }
   };
 
-  // Prologue: all three ring stages in flight.  In the loop, the fragments of
-  // the next k-step are read before the MFMAs of the current one; the
-  // k-tile barrier sits inside the last k-step, after every fragment of the
-  // tile is in registers, so it also frees that tile's stage for the tile
-  // three ahead (two tiles stay in flight).
+  // Prologue: the whole ring in flight.  In the loop, the fragments of the
+  // next k-step are read before the MFMAs of the current one; the barrier of
+  // step kt sits after every fragment of the step is in registers, so it also
+  // frees that step's stage for step kt + S.
   int pro = 0;
 #pragma unroll
-  for (int t = 0; t < S2; ++t)
+  for (int t = 0; t < S; ++t)
     if (t < nk) {
       issue(t);
       ++pro;
     }
-  if (pro >= 3) wait_vmcnt<2 * IPW>();
-  else if (pro == 2) wait_vmcnt<IPW>();
-  else wait_vmcnt<0>();
+  wait_vmcnt_le<IPW>((pro - 1) * IPW);
   barrier_lds();
   bf16x8 xa[4], wa[2], xb[4], wb[2];
   load_frags(0, 0, xa, wa);
@@ -330,15 +364,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_dma_kernel(const GemmBf16Params
   for (int kt = 0; kt < nk; ++kt) {
     load_frags(kt, 1, xb, wb);
     mfmas(xa, wa);
-    load_frags(kt, 2, xa, wa);
-    mfmas(xb, wb);
-    load_frags(kt, 3, xb, wb);
-    mfmas(xa, wa);
     if (kt + 1 < nk) {
-      // tile kt+1 landed once at most min(1, nk-2-kt) newer tiles are in flight
-      if (kt + 2 < nk) wait_vmcnt<IPW>(); else wait_vmcnt<0>();
-      barrier_lds();                     // every wave holds all of tile kt: its stage is free
-      if (kt + S2 < nk) issue(kt + S2);  // into the stage of tile kt
+      // step kt+1 landed once at most min(S-2, nk-2-kt) newer steps are in flight
+      wait_vmcnt_le<IPW>(min(S - 2, nk - 2 - kt) * IPW);
+      barrier_lds();                    // every wave holds all of step kt: its stage is free
+      if (kt + S < nk) issue(kt + S);   // into the stage of step kt
       load_frags(kt + 1, 0, xa, wa);
     }
     mfmas(xb, wb);
@@ -367,16 +397,30 @@ __global__ __launch_bounds__(256) void gemm_bf16_dma_kernel(const GemmBf16Params
 
 }  // namespace
 
+#ifndef ATTN_GEMM_S
+#define ATTN_GEMM_S 4
+#endif
+
+bool gemm_bf16_main_supported(const GemmBf16Params& p) {
+  // whole 256-column tiles inside one panel, K in 32-steps, and per-tile
+  // buffer ranges within 32-bit offsets
+  return p.n_panel % N2 == 0 && p.N % N2 == 0 && p.K % K2 == 0 && (int64_t)M2 * p.lda * 2 < 0x7fffffffLL &&
+         (int64_t)p.K * p.n_panel * 2 < 0x7fffffffLL;
+}
+
 hipError_t launch_gemm_bf16(const GemmBf16Params& p, hipStream_t stream) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
-  // main kernel: whole 128-column tiles inside one panel, K in 64-steps, and
-  // per-tile buffer ranges within 32-bit offsets
-  if (p.n_panel % N2 == 0 && p.N % N2 == 0 && p.K % K2 == 0 &&
-      (int64_t)M2 * p.lda * 2 < 0x7fffffffLL && (int64_t)p.K * p.n_panel * 2 < 0x7fffffffLL) {
+  if (gemm_bf16_main_supported(p)) {
     const int64_t tiles = (int64_t)((p.M + M2 - 1) / M2) * (p.N / N2);
-    hipLaunchKernelGGL(gemm_bf16_dma_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, p);
+    if (p.b_kmajor)
+      hipLaunchKernelGGL((gemm_bf16_dma_kernel<ATTN_GEMM_S, true>), dim3((unsigned)tiles), dim3(64 * NWAVES),
+                         0, stream, p);
+    else
+      hipLaunchKernelGGL((gemm_bf16_dma_kernel<ATTN_GEMM_S, false>), dim3((unsigned)tiles), dim3(64 * NWAVES),
+                         0, stream, p);
     return hipGetLastError();
   }
+  if (p.b_kmajor) return hipErrorInvalidValue;   // transposed panels: main kernel only
   const int64_t tiles = (int64_t)((p.M + BM - 1) / BM) * ((p.N + BNt - 1) / BNt);
   hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)tiles), dim3(NT), 0, stream, p);
   return hipGetLastError();

@@ -53,6 +53,7 @@ struct GemmBf16Params {
   int64_t lda, ldc;
   int M, N, K;
   int n_panel;                  // columns per B panel (N = panels * n_panel)
+  int b_kmajor;                 // 0: panels row-major [K, n_panel]; 1: transposed, [n_panel, K] (row stride K)
 };
 
 // Launchers: return hipSuccess or the launch error.  Shapes are validated by
@@ -60,6 +61,7 @@ struct GemmBf16Params {
 hipError_t launch_sdpa_bf16(const SdpaBf16Params& p, hipStream_t stream);
 hipError_t launch_sdpa_f32(const SdpaF32Params& p, hipStream_t stream);
 hipError_t launch_gemm_bf16(const GemmBf16Params& p, hipStream_t stream);
+bool gemm_bf16_main_supported(const GemmBf16Params& p);   // shapes the fast kernel takes
 
 // Queries per workgroup of the bf16 SDPA kernel chosen for these sizes.
 int sdpa_bf16_block_m(int batch, int heads, int n_q);
