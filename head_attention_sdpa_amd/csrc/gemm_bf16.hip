@@ -230,7 +230,8 @@ __device__ __forceinline__ int swz_w(int r) { return 4 * (r & 3); }
 
 template <int S, bool BT>
 __global__ __launch_bounds__(64 * NWAVES) void gemm_bf16_dma_kernel(const GemmBf16Params p) {
-  static_assert(S >= 2 && S <= 5, "bad configuration");
+  static_assert(S >= 4 && S <= 5, "bad configuration");
+  static_assert(S * STAGE >= M2 * N2, "the output tile must fit the ring");
   __shared__ __attribute__((aligned(1024))) __bf16 smem[S * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -374,14 +375,17 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_bf16_dma_kernel(const GemmBf
     mfmas(xb, wb);
   }
 
-  // acc[nb][mb] register r -> n = n0 + 64*wn + 32*nb + 8*(r/4) + 4*g + r%4,
-  //                           m = m0 + 128*wm + 32*mb + lane%32
-  __bf16* C = reinterpret_cast<__bf16*>(p.c);
+  // Epilogue through LDS (the ring is idle once every wave is past the last
+  // step): the tile is staged as [256 m][256 n] bf16, 512-byte rows, 16-byte
+  // chunk q of row m at position q ^ (m & 31), then written out as whole rows,
+  // 16 bytes per lane, 1 KiB per store instruction.
+  // acc[nb][mb] register r -> n = 64*wn + 32*nb + 8*(r/4) + 4*g + r%4,
+  //                           m = 128*wm + 32*mb + lane%32 (inside the tile)
+  barrier_lds();
+  __bf16* Cs = smem;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    const int m = m0 + wm * 128 + mb * 32 + l32;
-    if (m >= p.M) continue;
-    __bf16* crow = C + (int64_t)m * p.ldc + n0 + 64 * wn;
+    const int ml = wm * 128 + mb * 32 + l32;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
@@ -389,8 +393,20 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_bf16_dma_kernel(const GemmBf
         bf16x4 w;
 #pragma unroll
         for (int t = 0; t < 4; ++t) w[t] = (__bf16)acc[nb][mb][4 * rg + t];
-        *reinterpret_cast<u32x2*>(crow + 32 * nb + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, w);
+        const int q = 8 * wn + 4 * nb + rg;
+        *reinterpret_cast<u32x2*>(Cs + ml * N2 + 8 * (q ^ (ml & 31)) + 4 * g) = __builtin_bit_cast(u32x2, w);
       }
+    }
+  }
+  barrier_lds();
+  __bf16* C = reinterpret_cast<__bf16*>(p.c);
+  const int c = lane & 31;
+#pragma unroll
+  for (int i = 0; i < M2 / 2 / NWAVES; ++i) {
+    const int row = 2 * (wave * (M2 / 2 / NWAVES) + i) + (lane >> 5);
+    if (m0 + row < p.M) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(Cs + row * N2 + 8 * (c ^ (row & 31)));
+      *reinterpret_cast<u32x4*>(C + (int64_t)(m0 + row) * p.ldc + n0 + 8 * c) = v;
     }
   }
 }
@@ -405,7 +421,8 @@ bool gemm_bf16_main_supported(const GemmBf16Params& p) {
   // whole 256-column tiles inside one panel, K in 32-steps, and per-tile
   // buffer ranges within 32-bit offsets
   return p.n_panel % N2 == 0 && p.N % N2 == 0 && p.K % K2 == 0 && (int64_t)M2 * p.lda * 2 < 0x7fffffffLL &&
-         (int64_t)p.K * p.n_panel * 2 < 0x7fffffffLL;
+         (int64_t)p.K * p.n_panel * 2 < 0x7fffffffLL && p.ldc % 8 == 0 &&
+         (reinterpret_cast<uintptr_t>(p.c) & 15) == 0;   // 16-byte output stores
 }
 
 hipError_t launch_gemm_bf16(const GemmBf16Params& p, hipStream_t stream) {
