@@ -334,24 +334,37 @@ void sdpa_fwd_bf16_d64(const SdpaBf16Params p) {
     l += rs;
   }
 
+  // Epilogue: O = O^T / l, rounded once to bf16; rows without a legal key or
+  // beyond the query length are zeros.  Each wave stages its 32 x 64 block in
+  // its own 4 KiB of the (now idle) ring -- 16-byte chunk c of row r at
+  // position c ^ (r & 7) -- and writes it out as whole 128-byte rows.
   const float lt = sum_with_partner(l);
-  if (qi < p.n_q) {
-    const bool valid = (qi < Lq) && (lt > 0.f);
-    const float inv = valid ? 1.f / lt : 0.f;
-    __bf16* orow = reinterpret_cast<__bf16*>(p.o) + b * p.os_b + h * p.os_h + (int64_t)qi * p.os_n;
+  const bool valid = (qi < Lq) && (lt > 0.f);
+  const float inv = valid ? 1.f / lt : 0.f;
+  barrier_lds();  // every wave is past its last read of the ring
+  __bf16* Os = smem + wave * 32 * D;
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      bf16x4 w0, w1;
+  for (int rg = 0; rg < 4; ++rg) {
+    bf16x4 w0, w1;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        w0[t] = (__bf16)(o0[4 * rg + t] * inv);
-        w1[t] = (__bf16)(o1[4 * rg + t] * inv);
-      }
-      *reinterpret_cast<u32x2*>(orow + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, w0);
-      *reinterpret_cast<u32x2*>(orow + 32 + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, w1);
+    for (int t = 0; t < 4; ++t) {
+      w0[t] = (__bf16)(o0[4 * rg + t] * inv);
+      w1[t] = (__bf16)(o1[4 * rg + t] * inv);
     }
-    if (p.lse && g == 0)
-      p.lse[((int64_t)b * p.heads + h) * p.n_q + qi] = valid ? (m + __log2f(lt)) * LN2 : -INFINITY;
+    *reinterpret_cast<u32x2*>(Os + i32 * D + 8 * (rg ^ (i32 & 7)) + 4 * g) = __builtin_bit_cast(u32x2, w0);
+    *reinterpret_cast<u32x2*>(Os + i32 * D + 8 * ((4 + rg) ^ (i32 & 7)) + 4 * g) = __builtin_bit_cast(u32x2, w1);
+  }
+  if (p.lse && g == 0 && qi < p.n_q)
+    p.lse[((int64_t)b * p.heads + h) * p.n_q + qi] = valid ? (m + __log2f(lt)) * LN2 : -INFINITY;
+  __bf16* Ob = reinterpret_cast<__bf16*>(p.o) + b * p.os_b + h * p.os_h;
+  const int c = lane & 7;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * i + (lane >> 3);
+    if (qw0 + r < p.n_q) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(Os + r * D + 8 * (c ^ (r & 7)));
+      *reinterpret_cast<u32x4*>(Ob + (int64_t)(qw0 + r) * p.os_n + 8 * c) = v;
+    }
   }
 }
 
