@@ -7,16 +7,17 @@
 // bf16 at the store.  B may be given as up to three column panels so that the
 // Q, K and V projections of self-attention run as one launch.
 //
-// The kernel computes the transpose D = B^T . A^T on MFMA 32x32x16 bf16:
+// Both kernels compute the transpose D = B^T . A^T on MFMA 32x32x16 bf16:
 //   A-operand (B^T rows = output columns n): read transposed from the
 //     row-major B tile in LDS with ds_read_b64_tr_b16;
 //   B-operand (A^T columns = output rows m): contiguous 16-byte LDS reads;
 //   accumulator lane l holds output row m = l%32 and four consecutive output
-//     columns per register group, so C is stored as 8-byte row segments.
-// Workgroup tile 128 (m) x 128 (n) x 64 (k), four waves in a 2x2 arrangement
-// of 64x64 wave tiles, A and B tiles double-buffered in LDS with one barrier
-// per k-step.  Rows m >= M and columns n >= N are zero-filled on load and not
-// stored; K must be a multiple of 64 and N a multiple of 8.
+//     columns per register group.
+// gemm_bf16_dma_kernel (panels a multiple of 256 wide, K a multiple of 32)
+// takes the projections of the attention block; gemm_bf16_kernel (128 x 128 x
+// 64 tiles staged through registers, any M, N a multiple of 8, K a multiple of
+// 64) takes every other shape.  Rows m >= M are zero-filled on load and not
+// stored.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -50,6 +51,11 @@ __device__ __forceinline__ bf16x4 tr_read(const __bf16* lds_elem) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// General-shape kernel: workgroup tile 128 (m) x 128 (n) x 64 (k), four waves
+// in a 2x2 arrangement of 64x64 wave tiles, A and B tiles loaded through
+// registers and double-buffered in LDS with one barrier per k-step; columns
+// n >= N are zero-filled on load and not stored.  C is stored as 8-byte row
+// segments.
 __global__ __launch_bounds__(NT) void gemm_bf16_kernel(const GemmBf16Params p) {
   __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (A_TILE + B_TILE)];
 
@@ -228,7 +234,7 @@ constexpr int IPW = STAGE * 2 / 1024 / NWAVES;   // 1 KiB DMA instructions per w
 __device__ __forceinline__ int swz_x(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int swz_w(int r) { return 4 * (r & 3); }
 
-template <int S, bool BT>
+template <int S>
 __global__ __launch_bounds__(64 * NWAVES) void gemm_bf16_dma_kernel(const GemmBf16Params p) {
   static_assert(S >= 4 && S <= 5, "bad configuration");
   static_assert(S * STAGE >= M2 * N2, "the output tile must fit the ring");
@@ -262,11 +268,8 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_bf16_dma_kernel(const GemmBf
   const int panel = n0 / p.n_panel;
   // (explicit selection keeps the kernel-argument array in scalar registers)
   const uint16_t* wpanel = panel == 0 ? p.b[0] : (panel == 1 ? p.b[1] : p.b[2]);
-  // BT: the panel is W^T, [n_panel][K]; the tile's 256 rows start at n0
-  const __bf16* Wb = reinterpret_cast<const __bf16*>(wpanel) +
-                     (BT ? (int64_t)(n0 - panel * p.n_panel) * p.K : (int64_t)(n0 - panel * p.n_panel));
-  const uint32_t w_bytes = BT ? (uint32_t)((int64_t)(N2 - 1) * p.K * 2 + (int64_t)p.K * 2)
-                              : (uint32_t)((int64_t)(p.K - 1) * p.n_panel * 2 + N2 * 2);
+  const __bf16* Wb = reinterpret_cast<const __bf16*>(wpanel) + (n0 - panel * p.n_panel);
+  const uint32_t w_bytes = (uint32_t)((int64_t)(p.K - 1) * p.n_panel * 2 + N2 * 2);
 
   // per-lane DMA offsets (relative to the k-step base).  Instruction u of a
   // stage: u < 16 copies X rows 16u..16u+15 (four 16-byte chunks each);
@@ -280,10 +283,6 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_bf16_dma_kernel(const GemmBf
       const int r = 16 * u + (lane >> 2);
       const int c = (lane & 3) ^ swz_x(r);
       off[i] = (uint32_t)(((int64_t)r * p.lda + c * 8) * 2);
-    } else if (BT) {   // W^T rows 16w..16w+15 (n), four 16-byte chunks of k each
-      const int r = 16 * (u - 16) + (lane >> 2);
-      const int c = (lane & 3) ^ swz_x(r);
-      off[i] = (uint32_t)(((int64_t)r * p.K + c * 8) * 2);
     } else {
       const int w = u - 16, half = w >> 3;
       const int r = 4 * (w & 7) + (lane >> 4);
@@ -294,7 +293,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_bf16_dma_kernel(const GemmBf
   const int nk = p.K / K2;
   auto issue = [&](int kt) {
     const i32x4 rx = make_rsrc(Xb + kt * K2, x_bytes > (uint32_t)(kt * K2 * 2) ? x_bytes - kt * K2 * 2 : 0u);
-    const int64_t w_adv = BT ? (int64_t)kt * K2 : (int64_t)kt * K2 * p.n_panel;
+    const int64_t w_adv = (int64_t)kt * K2 * p.n_panel;
     const i32x4 rw = make_rsrc(Wb + w_adv, (uint32_t)((int64_t)w_bytes - w_adv * 2));
     __bf16* st = smem + (kt % S) * STAGE;
 #pragma unroll
@@ -302,8 +301,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_bf16_dma_kernel(const GemmBf
       const int u = wave * IPW + i;   // wave-uniform: selects, no branches
       const bool x = u < 16;
       const int w = u - 16;
-      dma16(off[i], x ? rx : rw,
-            lds_addr(st + (x ? u * 512 : X_SLICE + (BT ? w * 512 : (w >> 3) * W_HALF + (w & 7) * 512))));
+      dma16(off[i], x ? rx : rw, lds_addr(st + (x ? u * 512 : X_SLICE + (w >> 3) * W_HALF + (w & 7) * 512)));
     }
   };
 
@@ -318,7 +316,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_bf16_dma_kernel(const GemmBf
   // (MFMA A operand, transposed reads of the row-major W slice)
   auto load_frags = [&](int kt, int ks, bf16x8 (&xf)[4], bf16x8 (&wf)[2]) {
     const __bf16* Xs = smem + (kt % S) * STAGE;
-    const __bf16* Ws = Xs + X_SLICE + (BT ? 0 : (wn >> 1) * W_HALF);
+    const __bf16* Ws = Xs + X_SLICE + (wn >> 1) * W_HALF;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int r = wm * 128 + mb * 32 + l32;
@@ -327,17 +325,11 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_bf16_dma_kernel(const GemmBf
     }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      if (BT) {   // W^T slice [256 n][32 k], same layout as X
-        const int r = 64 * wn + 32 * nb + l32;
-        const int c = 2 * ks + g;
-        wf[nb] = *reinterpret_cast<const bf16x8*>(Ws + r * K2 + 8 * (c ^ swz_x(r)));
-      } else {
-        const int c = 8 * (wn & 1) + 4 * nb + tr_chunk;
-        const int r0 = 16 * ks + tr_row, r1 = r0 + 4;
-        const bf16x4 lo = tr_read(Ws + r0 * 128 + 8 * (c ^ swz_w(r0)) + tr_half);
-        const bf16x4 hi = tr_read(Ws + r1 * 128 + 8 * (c ^ swz_w(r1)) + tr_half);
-        wf[nb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
+      const int c = 8 * (wn & 1) + 4 * nb + tr_chunk;
+      const int r0 = 16 * ks + tr_row, r1 = r0 + 4;
+      const bf16x4 lo = tr_read(Ws + r0 * 128 + 8 * (c ^ swz_w(r0)) + tr_half);
+      const bf16x4 hi = tr_read(Ws + r1 * 128 + 8 * (c ^ swz_w(r1)) + tr_half);
+      wf[nb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   };
 
@@ -413,9 +405,7 @@ __global__ __launch_bounds__(64 * NWAVES) void gemm_bf16_dma_kernel(const GemmBf
 
 }  // namespace
 
-#ifndef ATTN_GEMM_S
-#define ATTN_GEMM_S 4
-#endif
+constexpr int kStages = 4;   // three 32-k steps in flight; the output tile reuses the 128 KiB ring
 
 bool gemm_bf16_main_supported(const GemmBf16Params& p) {
   // whole 256-column tiles inside one panel, K in 32-steps, and per-tile
@@ -429,15 +419,10 @@ hipError_t launch_gemm_bf16(const GemmBf16Params& p, hipStream_t stream) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
   if (gemm_bf16_main_supported(p)) {
     const int64_t tiles = (int64_t)((p.M + M2 - 1) / M2) * (p.N / N2);
-    if (p.b_kmajor)
-      hipLaunchKernelGGL((gemm_bf16_dma_kernel<ATTN_GEMM_S, true>), dim3((unsigned)tiles), dim3(64 * NWAVES),
-                         0, stream, p);
-    else
-      hipLaunchKernelGGL((gemm_bf16_dma_kernel<ATTN_GEMM_S, false>), dim3((unsigned)tiles), dim3(64 * NWAVES),
-                         0, stream, p);
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<kStages>), dim3((unsigned)tiles), dim3(64 * NWAVES), 0, stream,
+                       p);
     return hipGetLastError();
   }
-  if (p.b_kmajor) return hipErrorInvalidValue;   // transposed panels: main kernel only
   const int64_t tiles = (int64_t)((p.M + BM - 1) / BM) * ((p.N + BNt - 1) / BNt);
   hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)tiles), dim3(NT), 0, stream, p);
   return hipGetLastError();

@@ -53,7 +53,6 @@ struct GemmBf16Params {
   int64_t lda, ldc;
   int M, N, K;
   int n_panel;                  // columns per B panel (N = panels * n_panel)
-  int b_kmajor;                 // 0: panels row-major [K, n_panel]; 1: transposed, [n_panel, K] (row stride K)
 };
 
 // Launchers: return hipSuccess or the launch error.  Shapes are validated by
