@@ -28,8 +28,8 @@ STATUS = {0: "ATTN_OK", -1: "ATTN_E_INVALID", -2: "ATTN_E_UNSUPPORTED", -3: "ATT
           -4: "ATTN_E_WORKSPACE", -5: "ATTN_E_HIP"}
 
 # every entry point that include/attn_sdpa.h declares
-EXPORTS = ("attn_sdpa_fwd", "attn_mha_workspace_bytes", "attn_mha_fwd", "attn_status_str",
-           "attn_abi_version")
+EXPORTS = ("attn_sdpa_fwd", "attn_mha_workspace_bytes", "attn_mha_fwd", "attn_linear_fwd",
+           "attn_status_str", "attn_abi_version")
 
 
 class AttnError(RuntimeError):
@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L.attn_mha_fwd.argtypes = [i, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp,
                                    ctypes.c_float, i, vp, vp, vp, ctypes.c_size_t, vp]
         L.attn_mha_fwd.restype = i
+        L.attn_linear_fwd.argtypes = [i, i, i, i, vp, ctypes.c_int64, vp, vp, ctypes.c_int64, vp]
+        L.attn_linear_fwd.restype = i
         L.attn_status_str.argtypes = [i]
         L.attn_status_str.restype = ctypes.c_char_p
         L.attn_abi_version.argtypes = []
@@ -182,4 +184,26 @@ def mha(x_q, x_kv, w_q, w_k, w_v, w_o, heads, scale=None, causal=False, seqlens_
                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                             _stream(stream))
     _check("attn_mha_fwd", rc)
+    return out
+
+
+def linear(x, w, out=None, stream=None):
+    """One projection y = x . w (no bias) on the GPU, bf16.  x [m, k] with a
+    contiguous last dimension (any row stride), w [k, n] contiguous; returns
+    y [m, n] (or writes `out`, any row stride)."""
+    torch = _torch()
+    if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[0]:
+        raise ValueError("expected x [m, k] and w [k, n]")
+    if x.stride(1) != 1 or not w.is_contiguous() or x.device != w.device or x.dtype != w.dtype:
+        raise ValueError("x needs a contiguous last dimension, w must be contiguous, same device and dtype")
+    m, k = x.shape
+    n = w.shape[1]
+    if out is None:
+        out = torch.empty((m, n), dtype=x.dtype, device=x.device)
+    if out.dim() != 2 or out.shape != (m, n) or out.stride(1) != 1 or out.dtype != x.dtype:
+        raise ValueError("out must be [m, n] with a contiguous last dimension")
+    rc = lib().attn_linear_fwd(_dtype_code(x), m, k, n, x.data_ptr() if m else None, max(x.stride(0), k),
+                               w.data_ptr() if m else None, out.data_ptr() if m else None,
+                               max(out.stride(0), n), _stream(stream))
+    _check("attn_linear_fwd", rc)
     return out

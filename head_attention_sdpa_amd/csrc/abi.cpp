@@ -285,4 +285,23 @@ int attn_mha_fwd(attn_dtype dt, int batch, int n_q, int n_kv, int d_model, int h
   return hip_status(attn::launch_gemm_bf16(go, stream));
 }
 
+int attn_linear_fwd(attn_dtype dt, int m, int k, int n, const void* x, int64_t ldx, const void* w,
+                    void* y, int64_t ldy, attn_stream_t stream_) {
+  if (dt != ATTN_F32 && dt != ATTN_BF16) return ATTN_E_INVALID;
+  if (m < 0 || k < 1 || n < 1 || ldx < k || ldy < n) return ATTN_E_INVALID;
+  if (dt != ATTN_BF16 || k % 64 != 0 || n % 8 != 0 || (int64_t)k * n * 2 >= 0x7fffffffLL)
+    return ATTN_E_UNSUPPORTED;
+  if (m == 0) return ATTN_OK;
+  if (!x || !w || !y) return ATTN_E_INVALID;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16) || ldx % 8 != 0 || ldy % 8 != 0)
+    return ATTN_E_ALIGN;
+  if (((int64_t)m + 127) / 128 * (((int64_t)n + 127) / 128) > kMaxGrid) return ATTN_E_UNSUPPORTED;
+  GemmBf16Params g = {};
+  g.a = static_cast<const uint16_t*>(x);
+  g.b[0] = static_cast<const uint16_t*>(w);
+  g.c = static_cast<uint16_t*>(y);
+  g.lda = ldx; g.ldc = ldy; g.M = m; g.N = n; g.K = k; g.n_panel = n;
+  return hip_status(attn::launch_gemm_bf16(g, static_cast<hipStream_t>(stream_)));
+}
+
 }  // extern "C"

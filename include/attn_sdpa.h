@@ -14,6 +14,9 @@
  *                  Self-attention passes x_kv == x_q; encoder-decoder
  *                  attention passes the encoder output as x_kv (section 3.2.3;
  *                  rockcohen.cc 5.3).
+ *   attn_linear_fwd one projection of that block on its own, Y = X.W (the
+ *                  products X W_i^Q, X W_i^K, X W_i^V and Concat(...) W^O of
+ *                  section 3.2.2; rockcohen.cc 5.2).
  *
  * Masking.  Key j is legal for query i iff j < L_kv[b] (when key lengths are
  * given) and, with ATTN_MASK_CAUSAL, j <= i (the decoder's illegal
@@ -46,7 +49,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 typedef void* attn_stream_t; /* hipStream_t */
 
@@ -136,6 +139,26 @@ int attn_mha_fwd(attn_dtype dt, int batch, int n_q, int n_kv, int d_model, int h
 
 /* Human-readable name of an attn_status value (static storage). */
 const char* attn_status_str(int status);
+
+/*
+ * attn_linear_fwd -- y = x . w, no bias (one projection of the multi-head
+ * block, section 3.2.2).
+ *
+ *   x   [m, k] bf16, row stride ldx elements (ldx >= k)
+ *   w   [k, n] bf16, row-major and contiguous (row stride n): Y = X.W as in
+ *       the projections of attn_mha_fwd
+ *   y   [m, n] bf16, row stride ldy elements (ldy >= n); the m x n block is
+ *       written in full, the rest of each row is not touched
+ *   dt  ATTN_BF16 only (ATTN_F32 gives ATTN_E_UNSUPPORTED): fp32 accumulation,
+ *       y rounded to bf16 once (round to nearest even).
+ *   m >= 0; k >= 1 and a multiple of 64; n >= 8 and a multiple of 8
+ *       (otherwise ATTN_E_UNSUPPORTED); k * n * 2 bytes below 2 GiB.
+ *   x, w, y 16-byte aligned and ldx, ldy multiples of 8 (ATTN_E_ALIGN).
+ *   x, w, y may be NULL when m = 0 (nothing is enqueued).
+ * y must not overlap x or w.  Returns ATTN_OK or a negative attn_status.
+ */
+int attn_linear_fwd(attn_dtype dt, int m, int k, int n, const void* x, int64_t ldx, const void* w,
+                    void* y, int64_t ldy, attn_stream_t stream);
 
 /* ATTN_ABI_VERSION of the loaded library. */
 int attn_abi_version(void);

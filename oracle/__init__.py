@@ -2,7 +2,8 @@
 
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
 and the ``cpu_baseline`` leg of ``bench.py``, never by the product package.
-It shares no code with the HIP path.
+It shares no code with the HIP path.  Functions: ``sdpa``, ``sdpa_rows``,
+``mha``, ``mha_rows``, ``linear`` and ``round_bf16``.
 
 The arithmetic lives in ``oracle.c`` (plain C, fp64, one query row at a time,
 sums in index order).  This module only marshals numpy arrays through ctypes.
@@ -55,9 +56,11 @@ def _load():
                                        _I, _I, i, i]
         lib.oracle_mha_rows_f64.argtypes = [i, i, i, i, i, i, i, _D, _D, _D, _D, _D, _D, _L,
                                             ctypes.c_int64, _D, d, i, _I, _I, i, i]
+        lib.oracle_linear_f64.argtypes = [i, i, i, _D, ctypes.c_int64, _L, ctypes.c_int64, _D, _D, i]
         lib.oracle_round_bf16.argtypes = [d]
         lib.oracle_round_bf16.restype = d
-        for f in ("oracle_sdpa_f64", "oracle_sdpa_rows_f64", "oracle_mha_f64", "oracle_mha_rows_f64"):
+        for f in ("oracle_sdpa_f64", "oracle_sdpa_rows_f64", "oracle_mha_f64", "oracle_mha_rows_f64",
+                  "oracle_linear_f64"):
             getattr(lib, f).restype = i
         _lib = lib
     return _lib
@@ -189,6 +192,27 @@ def mha_rows(x_q, x_kv, w_q, w_k, w_v, w_o, heads, rows, scale=None, causal=Fals
                                      int(bool(causal)), plq, plk, int(bool(bf16_storage)),
                                      nthreads or default_threads())
     _check(rc, "oracle_mha_rows_f64")
+    return y
+
+
+def linear(x, w, rows=None, nthreads=None):
+    """One projection of the multi-head block in fp64, y = x . w (no bias;
+    paper section 3.2.2).  x [M_x, K], w [K, N] row-major; rows (optional)
+    selects the rows of x to compute.  Returns y [len(rows) or M_x, N]."""
+    x, w = _f64(x), _f64(w)
+    mx, k = x.shape
+    k2, n = w.shape
+    if k != k2:
+        raise ValueError("inner dimensions differ")
+    prow = None
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        prow = rows.ctypes.data_as(_L)
+    m = mx if rows is None else len(rows)
+    y = np.empty((m, n))
+    rc = _load().oracle_linear_f64(m, k, n, _ptr(x), k, prow, mx, _ptr(w), _ptr(y),
+                                   nthreads or default_threads())
+    _check(rc, "oracle_linear_f64")
     return y
 
 

@@ -10,7 +10,8 @@
  *       section 5.1), and
  *   (2) multi-head attention, MultiHead = Concat(head_1..head_h) W^O with
  *       head_i = Attention(Q W_i^Q, K W_i^K, V W_i^V) (paper section 3.2.2; the
- *       vlmlib.cn summary and rockcohen.cc section 5.2).
+ *       vlmlib.cn summary and rockcohen.cc section 5.2), and
+ *   (3) one projection of that block, y = x . W (no bias).
  *
  * Definitions followed literally, one query row at a time:
  *   legal(j)  <=>  j < n_kv  and  (no key lengths or j < L_kv[b])
@@ -222,6 +223,22 @@ static void gemm_range(void* p, int64_t begin, int64_t end, double* unused) {
     }
     if (g->round_out) for (int n = 0; n < g->N; ++n) c[n] = round_bf16(c[n]);
   }
+}
+
+/* One projection of the multi-head block, y = x . w (no bias): the products
+ * X W_i^Q, X W_i^K, X W_i^V and Concat(head_1..h) W^O of the paper's section
+ * 3.2.2 all have this form.  x rows have stride x_stride; rows (NULL or
+ * [M]) selects which rows of x produce the M rows of y; w is row-major
+ * [K][N]; y is [M][N]. */
+int oracle_linear_f64(int M, int K, int N, const double* x, int64_t x_stride, const int64_t* rows,
+                      int64_t x_rows, const double* w, double* y, int nthreads) {
+  if (M < 0 || K < 0 || N < 0 || x_stride < K || x_rows < 0) return ORACLE_EINVAL;
+  if (rows)
+    for (int64_t r = 0; r < M; ++r)
+      if (rows[r] < 0 || rows[r] >= x_rows) return ORACLE_EINVAL;
+  if (!rows && M > x_rows) return ORACLE_EINVAL;
+  gemm_ctx g = {x, x_stride, rows, w, K, N, y, 0};
+  return parallel_for(M, nthreads, 0, gemm_range, &g);
 }
 
 /* ---- multi-head attention ------------------------------------------------ */

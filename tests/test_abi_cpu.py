@@ -108,3 +108,29 @@ def test_mha_workspace_bytes():
     assert L.attn_mha_workspace_bytes(0, 4, 4096, 4096, 1024, 16, 64, 64) == 0  # f32 unsupported
     assert L.attn_mha_workspace_bytes(1, 4, 4096, 4096, 1000, 16, 64, 64) == 0
     assert L.attn_mha_workspace_bytes(1, 0, 4096, 4096, 1024, 16, 64, 64) == 0
+
+
+def linear_call(dt=1, m=64, k=128, n=256, x=FAKE, ldx=128, w=FAKE, y=FAKE, ldy=256):
+    return attn.lib().attn_linear_fwd(dt, m, k, n, x, ldx, w, y, ldy, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=5), -1),
+    (dict(m=-1), -1),
+    (dict(k=0), -1),
+    (dict(n=0), -1),
+    (dict(ldx=64), -1),
+    (dict(ldy=128), -1),
+    (dict(x=None), -1),
+    (dict(w=None), -1),
+    (dict(y=None), -1),
+    (dict(dt=0), -2),
+    (dict(k=96, ldx=96), -2),
+    (dict(n=12, ldy=16), -2),
+    (dict(x=MISALIGNED), -3),
+    (dict(y=MISALIGNED), -3),
+    (dict(ldx=132), -3),
+    (dict(m=0, x=None, w=None, y=None), 0),   # nothing to do: no launch
+])
+def test_linear_validation(kw, code):
+    assert linear_call(**kw) == code

@@ -331,3 +331,38 @@ def test_mha_bf16_storage_mode_is_close_but_distinct():
     yr = oracle.mha(xq, xkv, wq, wk, wv, wo, heads=h, bf16_storage=True)
     d = np.abs(yr - y).max()
     assert 0 < d < 0.05
+
+
+# ---------------------------------------------------------------------------
+# One projection, y = x . W (paper section 3.2.2: X W_i^Q, X W_i^K, X W_i^V
+# and Concat(...) W^O), which the library also exposes on its own
+# ---------------------------------------------------------------------------
+def test_linear_closed_form():
+    """x[m, k] = m + 1 and w[k, n] = k + n give y[m, n] = (m + 1) (K(K-1)/2 + nK)
+    exactly.  Catches a transposed weight (w[n][k] reads k + n too, so the
+    non-square shape below is what separates them: K = 7, N = 3), a dropped or
+    repeated term, and a row offset."""
+    M, K, N = 4, 7, 3
+    x = np.array([[m + 1.0] * K for m in range(M)])
+    w = np.array([[k + n + 0.0 for n in range(N)] for k in range(K)])
+    y = oracle.linear(x, w)
+    ref = np.array([[(m + 1) * (K * (K - 1) / 2 + n * K) for n in range(N)] for m in range(M)])
+    assert np.array_equal(y, ref)
+
+
+def test_linear_special_cases():
+    """Identity weights return x; a one-hot column of W copies one column of x
+    (on a non-square W, so a transposed weight fails); zero weights give zeros;
+    the row selection returns the selected rows of the full product."""
+    x = rnd(302, (6, 8))
+    assert np.array_equal(oracle.linear(x, np.eye(8)), x)
+    w = np.zeros((8, 3))
+    w[5, 1] = 1.0
+    w[2, 2] = -2.0
+    y = oracle.linear(x, w)
+    assert np.array_equal(y[:, 0], np.zeros(6))
+    assert np.array_equal(y[:, 1], x[:, 5])
+    assert np.array_equal(y[:, 2], -2.0 * x[:, 2])
+    w2 = rnd(303, (8, 5))
+    full = oracle.linear(x, w2)
+    assert np.array_equal(oracle.linear(x, w2, rows=[4, 0, 4]), full[[4, 0, 4]])
