@@ -22,17 +22,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_common.h"
 #include "internal.h"
 
 namespace attn {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 128, BNt = 128, BK = 64;
 constexpr int A_ROW = BK + 8;        // 72 bf16 = 144 B per A row in LDS
@@ -40,16 +35,6 @@ constexpr int B_ROW = BNt + 16;      // 144 bf16 = 288 B per B row in LDS
 constexpr int A_TILE = BM * A_ROW;
 constexpr int B_TILE = BK * B_ROW;
 constexpr int NT = 256;
-
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x4 tr_read(const __bf16* lds_elem) {
-  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_elem));
-  return __builtin_bit_cast(bf16x4, v);
-}
 
 // General-shape kernel: workgroup tile 128 (m) x 128 (n) x 64 (k), four waves
 // in a 2x2 arrangement of 64x64 wave tiles, A and B tiles loaded through
@@ -191,39 +176,6 @@ __global__ __launch_bounds__(NT) void gemm_bf16_kernel(const GemmBf16Params p) {
 //     c ^ ((r>>2)&3) (16 consecutive rows read one chunk each: distinct banks)
 //   W slice, two halves of [32 k][128 n]: chunk c of row r at position
 //     c ^ (4*(r&3)) (transposed reads touch 4 consecutive rows x 2 or 4 chunks)
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
-  // the descriptor must live in scalar registers: all inputs are wave-uniform
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
-               __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff),
-               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
-}
-__device__ __forceinline__ void dma16(uint32_t voff, i32x4 rsrc, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               ::"v"(voff), "s"(rsrc), "s"(lds_addr) : "memory", "m0");
-}
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// wait until at most n (a multiple of Step, n <= 4*Step) DMA instructions are in flight
-template <int Step>
-__device__ __forceinline__ void wait_vmcnt_le(int n) {
-  if (n <= 0) wait_vmcnt<0>();
-  else if (n <= Step) wait_vmcnt<Step>();
-  else if (n <= 2 * Step) wait_vmcnt<2 * Step>();
-  else if (n <= 3 * Step) wait_vmcnt<3 * Step>();
-  else wait_vmcnt<4 * Step>();
-}
-__device__ __forceinline__ void barrier_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)reinterpret_cast<uintptr_t>(p);
-}
-
 constexpr int M2 = 256, N2 = 256, K2 = 32;
 constexpr int X_SLICE = M2 * K2;         // bf16 elements (16 KiB)
 constexpr int W_HALF = K2 * 128;         // one [32 k][128 n] half of the W slice (8 KiB)

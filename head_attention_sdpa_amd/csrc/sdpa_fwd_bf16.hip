@@ -22,57 +22,21 @@
 //   of the second product without any data movement.  V stays row-major in
 //   LDS; its transposed operand is read with ds_read_b64_tr_b16.
 //
-// MFMA lane layouts (v_mfma_f32_32x32x16_bf16; checked by a probe on gfx950):
-//   A[32 x 16]: lane l holds row l%32, k = 8*(l/32) + 0..7
-//   B[16 x 32]: lane l holds col l%32, k = 8*(l/32) + 0..7
-//   C[32 x 32]: lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4, col l%32
-// ds_read_b64_tr_b16, per group of 16 lanes where lane k points at 4 values
-// M[k][0..3]: lane i receives M[i/4][i%4], M[4+i/4][i%4], M[8+i/4][i%4],
-// M[12+i/4][i%4].
+// The MFMA and transposed-read lane layouts are listed in device_common.h.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
+#include "device_common.h"
 #include "internal.h"
 
 namespace attn {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 constexpr int D = 64;         // head size (d_k = d_v)
 constexpr int BN = 64;        // keys per iteration
 constexpr float LN2 = 0.69314718055994530942f;
-
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// Value held by lane l^32, combined with the own value: {own, partner}.
-__device__ __forceinline__ float max_with_partner(float x) {
-  uint32_t u = __float_as_uint(x);
-  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_with_partner(float x) {
-  uint32_t u = __float_as_uint(x);
-  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ bf16x4 tr_read(const __bf16* lds_elem) {
-  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_elem));
-  return __builtin_bit_cast(bf16x4, v);
-}
 
 // Workgroup id -> (batch*head index, query block).  Workgroups are handed to
 // the 8 XCDs round-robin, so when batch*heads is a multiple of 8 all query
@@ -100,48 +64,6 @@ __device__ __forceinline__ void map_block(int bid, int bh_total, int nqb, int ca
 __device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int swz_v(int r) { return ((r >> 1) & 1) << 2; }
 
-// Global -> LDS copies (16 bytes per lane, lane i lands at M0 + 16*i) are
-// issued from inline assembly and waited for explicitly with vmcnt: the
-// compiler then never inserts its own conservative "all DMA done" waits in
-// front of LDS reads, which would drain the prefetch ring every iteration.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor: 48-bit base, stride 0, range in bytes; reads at or
-// past the range return zeros.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
-  // the descriptor must live in scalar registers: all inputs are wave-uniform
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
-               __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff),
-               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
-}
-
-__device__ __forceinline__ void dma16(uint32_t voff, i32x4 rsrc, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               ::"v"(voff), "s"(rsrc), "s"(lds_addr) : "memory", "m0");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// wait until at most n (a multiple of Step, n <= 4*Step) DMA instructions are in flight
-template <int Step>
-__device__ __forceinline__ void wait_vmcnt_le(int n) {
-  if (n <= 0) wait_vmcnt<0>();
-  else if (n <= Step) wait_vmcnt<Step>();
-  else if (n <= 2 * Step) wait_vmcnt<2 * Step>();
-  else if (n <= 3 * Step) wait_vmcnt<3 * Step>();
-  else wait_vmcnt<4 * Step>();
-}
-// The wave's own LDS reads are complete, then all waves meet.
-__device__ __forceinline__ void barrier_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)reinterpret_cast<uintptr_t>(p);
-}
 
 // One workgroup = (batch, head, 32*NW queries); wave w owns queries
 // 32w..32w+31 of the block.  Per key tile the workgroup waits for its DMA,
