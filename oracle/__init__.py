@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
 and the ``cpu_baseline`` leg of ``bench.py``, never by the product package.
 It shares no code with the HIP path.  Functions: ``sdpa``, ``sdpa_rows``,
-``mha``, ``mha_rows``, ``linear`` and ``round_bf16``.
+``mha``, ``mha_rows``, ``linear``, ``decode`` and ``round_bf16``.
 
 The arithmetic lives in ``oracle.c`` (plain C, fp64, one query row at a time,
 sums in index order).  This module only marshals numpy arrays through ctypes.
@@ -56,11 +56,12 @@ def _load():
                                        _I, _I, i, i]
         lib.oracle_mha_rows_f64.argtypes = [i, i, i, i, i, i, i, _D, _D, _D, _D, _D, _D, _L,
                                             ctypes.c_int64, _D, d, i, _I, _I, i, i]
+        lib.oracle_decode_f64.argtypes = [i, i, i, i, i, i, _D, _D, _D, _D, _D, d, _I, i]
         lib.oracle_linear_f64.argtypes = [i, i, i, _D, ctypes.c_int64, _L, ctypes.c_int64, _D, _D, i]
         lib.oracle_round_bf16.argtypes = [d]
         lib.oracle_round_bf16.restype = d
         for f in ("oracle_sdpa_f64", "oracle_sdpa_rows_f64", "oracle_mha_f64", "oracle_mha_rows_f64",
-                  "oracle_linear_f64"):
+                  "oracle_linear_f64", "oracle_decode_f64"):
             getattr(lib, f).restype = i
         _lib = lib
     return _lib
@@ -193,6 +194,25 @@ def mha_rows(x_q, x_kv, w_q, w_k, w_v, w_o, heads, rows, scale=None, causal=Fals
                                      nthreads or default_threads())
     _check(rc, "oracle_mha_rows_f64")
     return y
+
+
+def decode(q, k, v, scale=None, seqlens_kv=None, nthreads=None):
+    """One decoding step over a key/value cache in fp64: the n_q queries are
+    the newest positions L_kv[b] - n_q + i of each sequence and attend to the
+    cache up to their own position (causal, aligned at the end of the cache).
+    q [B,H,n_q,d_k], k [B,H,n_kv,d_k], v [B,H,n_kv,d_v]; seqlens_kv [B] or
+    None (= n_kv).  Returns (o [B,H,n_q,d_v], lse [B,H,n_q])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, n_q, d_k = q.shape
+    n_kv, d_v = k.shape[2], v.shape[3]
+    scale = 1.0 / math.sqrt(d_k) if scale is None else float(scale)
+    o = np.empty((B, H, n_q, d_v))
+    lse = np.empty((B, H, n_q))
+    lk, plk = _lens(seqlens_kv, B)
+    rc = _load().oracle_decode_f64(B, H, n_q, n_kv, d_k, d_v, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                   _ptr(lse), scale, plk, nthreads or default_threads())
+    _check(rc, "oracle_decode_f64")
+    return o, lse
 
 
 def linear(x, w, rows=None, nthreads=None):

@@ -11,7 +11,9 @@
  *   (2) multi-head attention, MultiHead = Concat(head_1..head_h) W^O with
  *       head_i = Attention(Q W_i^Q, K W_i^K, V W_i^V) (paper section 3.2.2; the
  *       vlmlib.cn summary and rockcohen.cc section 5.2), and
- *   (3) one projection of that block, y = x . W (no bias).
+ *   (3) one projection of that block, y = x . W (no bias), and
+ *   (4) one decoding step over a key/value cache (the newest n_q positions of
+ *       each sequence under the causal mask).
  *
  * Definitions followed literally, one query row at a time:
  *   legal(j)  <=>  j < n_kv  and  (no key lengths or j < L_kv[b])
@@ -146,6 +148,7 @@ typedef struct {
   const double *q, *k, *v; double *o, *lse;
   const int *seqlens_q, *seqlens_kv;
   const int64_t* rows;   /* NULL: row r is flat index r; else rows[r] is the flat index */
+  int decode;            /* 1: query i is sequence position L_kv[b] - n_q + i (see below) */
 } sdpa_ctx;
 
 static void sdpa_range(void* p, int64_t begin, int64_t end, double* s) {
@@ -167,8 +170,14 @@ static void sdpa_range(void* p, int64_t begin, int64_t end, double* s) {
     const double* q = c->q + flat * c->d_k;
     const double* K = c->k + bh * c->n_kv * c->d_k;
     const double* V = c->v + bh * c->n_kv * c->d_v;
+    int causal_i = c->causal ? i : -1;
+    if (c->decode) {                                  /* the last n_q positions of the sequence */
+      int pos = legal_end - c->n_q + i;
+      if (pos < 0) legal_end = 0;                     /* before the sequence: no legal key */
+      else causal_i = pos;
+    }
     sdpa_row(q, K, c->d_k, V, c->d_v, c->n_kv, c->d_k, c->d_v, c->scale, legal_end,
-             c->causal ? i : -1, s, out, lse);
+             causal_i, s, out, lse);
   }
 }
 
@@ -185,7 +194,25 @@ int oracle_sdpa_f64(int B, int H, int n_q, int n_kv, int d_k, int d_v, const dou
                     int causal, const int* seqlens_q, const int* seqlens_kv, int nthreads) {
   if (B < 0 || H < 0 || n_q < 0 || n_kv < 0 || d_k < 1 || d_v < 1 || !(scale > 0.0)) return ORACLE_EINVAL;
   if (!check_lengths(seqlens_q, B, n_q) || !check_lengths(seqlens_kv, B, n_kv)) return ORACLE_EINVAL;
-  sdpa_ctx c = {B, H, n_q, n_kv, d_k, d_v, scale, causal, q, k, v, o, lse, seqlens_q, seqlens_kv, NULL};
+  sdpa_ctx c = {B, H, n_q, n_kv, d_k, d_v, scale, causal, q, k, v, o, lse, seqlens_q, seqlens_kv, NULL, 0};
+  return parallel_for((int64_t)B * H * n_q, nthreads, n_kv > 0 ? n_kv : 1, sdpa_range, &c);
+}
+
+/* One decoding step over a key/value cache: the n_q queries are the newest
+ * n_q positions of each sequence, L_kv[b] - n_q + i for query i (L_kv = n_kv
+ * when no lengths are given), and each attends to the cache up to and
+ * including its own position -- the decoder's causal mask of section 3.2.3
+ * (rockcohen.cc 5.3) applied to the last rows only, as autoregressive
+ * generation evaluates it one step at a time (attention-paper-guide sections
+ * 05 and 07+, misconception 03; the vlmlib.cn summary's training-objective
+ * paragraph; the csdn blog, section 3.6).  A query whose position is negative
+ * (L_kv[b] < n_q) has no legal key: O = 0, lse = -inf. */
+int oracle_decode_f64(int B, int H, int n_q, int n_kv, int d_k, int d_v, const double* q,
+                      const double* k, const double* v, double* o, double* lse, double scale,
+                      const int* seqlens_kv, int nthreads) {
+  if (B < 0 || H < 0 || n_q < 0 || n_kv < 0 || d_k < 1 || d_v < 1 || !(scale > 0.0)) return ORACLE_EINVAL;
+  if (!check_lengths(seqlens_kv, B, n_kv)) return ORACLE_EINVAL;
+  sdpa_ctx c = {B, H, n_q, n_kv, d_k, d_v, scale, 0, q, k, v, o, lse, NULL, seqlens_kv, NULL, 1};
   return parallel_for((int64_t)B * H * n_q, nthreads, n_kv > 0 ? n_kv : 1, sdpa_range, &c);
 }
 
@@ -199,7 +226,7 @@ int oracle_sdpa_rows_f64(int B, int H, int n_q, int n_kv, int d_k, int d_v, cons
   if (!check_lengths(seqlens_q, B, n_q) || !check_lengths(seqlens_kv, B, n_kv)) return ORACLE_EINVAL;
   for (int64_t r = 0; r < nrows; ++r)
     if (rows[r] < 0 || rows[r] >= (int64_t)B * H * n_q) return ORACLE_EINVAL;
-  sdpa_ctx c = {B, H, n_q, n_kv, d_k, d_v, scale, causal, q, k, v, o, lse, seqlens_q, seqlens_kv, rows};
+  sdpa_ctx c = {B, H, n_q, n_kv, d_k, d_v, scale, causal, q, k, v, o, lse, seqlens_q, seqlens_kv, rows, 0};
   return parallel_for(nrows, nthreads, n_kv > 0 ? n_kv : 1, sdpa_range, &c);
 }
 

@@ -31,6 +31,8 @@ MUTATIONS = {
                               "ocat + (int64_t)(c->H - 1 - h) * c->d_v, NULL);"),
     "value row shifted": ("const double* vj = V + (int64_t)j * v_stride;",
                           "const double* vj = V + (int64_t)(j == 0 ? 0 : j - 1) * v_stride;"),
+    "decode alignment off by one": ("int pos = legal_end - c->n_q + i;", "int pos = legal_end - c->n_q + i + 1;"),
+    "decode aligned at the start": ("int pos = legal_end - c->n_q + i;", "int pos = i;"),
     "projection weight transposed": ("for (int n = 0; n < g->N; ++n) c[n] += ak * wk[n];",
                                      "for (int n = 0; n < g->N; ++n) c[n] += ak * g->w[(int64_t)n * g->K + kk];"),
 }

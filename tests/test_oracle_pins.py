@@ -366,3 +366,55 @@ def test_linear_special_cases():
     w2 = rnd(303, (8, 5))
     full = oracle.linear(x, w2)
     assert np.array_equal(oracle.linear(x, w2, rows=[4, 0, 4]), full[[4, 0, 4]])
+
+
+# ---------------------------------------------------------------------------
+# One decoding step over a key/value cache (autoregressive generation:
+# attention-paper-guide sections 05 and 07+, the csdn blog section 3.6)
+# ---------------------------------------------------------------------------
+def test_decode_last_rows_equal_full_causal_attention():
+    """Generating one step at a time reproduces the decoder's masked attention:
+    the newest n_q queries over the full cache give exactly the last n_q rows
+    of causal self-attention over the whole sequence (the mask of rockcohen.cc
+    5.3).  Catches an off-by-one or reversed alignment of the positions."""
+    B, H, n, d, n_q = 2, 3, 23, 8, 4
+    q, k, v = rnd(400, (B, H, n, d)), rnd(401, (B, H, n, d)), rnd(402, (B, H, n, d))
+    o_full, lse_full = oracle.sdpa(q, k, v, causal=True)
+    o, lse = oracle.decode(q[:, :, n - n_q:], k, v)
+    assert np.array_equal(o, o_full[:, :, n - n_q:])
+    assert np.array_equal(lse, lse_full[:, :, n - n_q:])
+
+
+def test_decode_single_query_is_unmasked_attention_over_the_cache():
+    """With one query the causal mask removes nothing inside the cache: the
+    step equals unmasked attention over the first L_kv keys (and ignores what
+    the cache holds beyond them, NaN included)."""
+    B, H, n_kv, d = 3, 2, 17, 8
+    q, k, v = rnd(410, (B, H, 1, d)), rnd(411, (B, H, n_kv, d)), rnd(412, (B, H, n_kv, d))
+    L = np.array([17, 9, 1], np.int32)
+    ref, ref_lse = oracle.sdpa(q, k, v, seqlens_kv=L)
+    for b in range(B):
+        k[b, :, L[b]:] = np.nan
+        v[b, :, L[b]:] = np.nan
+    o, lse = oracle.decode(q, k, v, seqlens_kv=L)
+    assert np.array_equal(o, ref) and np.array_equal(lse, ref_lse)
+
+
+def test_decode_per_sequence_lengths_and_short_sequences():
+    """With cache lengths L_b the newest queries sit at L_b - n_q + i: equal to
+    causal attention over the truncated sequence.  A sequence shorter than n_q
+    leaves its first n_q - L_b queries without keys: zeros and -inf."""
+    B, H, n_kv, d, n_q = 3, 2, 20, 8, 3
+    q, k, v = rnd(420, (B, H, n_q, d)), rnd(421, (B, H, n_kv, d)), rnd(422, (B, H, n_kv, d))
+    L = np.array([20, 11, 2], np.int32)
+    o, lse = oracle.decode(q, k, v, seqlens_kv=L)
+    for b in range(2):
+        Lb = int(L[b])
+        qq = np.concatenate([np.zeros((1, H, Lb - n_q, d)), q[b:b + 1]], axis=2)
+        of, lf = oracle.sdpa(qq, k[b:b + 1, :, :Lb], v[b:b + 1, :, :Lb], causal=True)
+        assert np.array_equal(o[b], of[0, :, Lb - n_q:])
+        assert np.array_equal(lse[b], lf[0, :, Lb - n_q:])
+    # L = 2 < n_q = 3: query 0 is position -1 (nothing), queries 1, 2 are positions 0, 1
+    assert np.all(o[2, :, 0] == 0.0) and np.all(lse[2, :, 0] == -np.inf)
+    of, lf = oracle.sdpa(q[2:3, :, 1:], k[2:3, :, :2], v[2:3, :, :2], causal=True)
+    assert np.array_equal(o[2, :, 1:], of[0]) and np.array_equal(lse[2, :, 1:], lf[0])
