@@ -251,3 +251,18 @@ def config(c: int, **overrides):
         inp.w_st = tuple(bf16_bits(w) for w in ws)
         return inp
     raise ValueError(c)
+
+
+def decode_workload(**overrides):
+    """One decoding step over a key/value cache (bf16, head size 64): B = 16
+    sequences x 16 heads (the big model's head count), one new query each, a
+    cache of capacity 4096 (the block's sequence length) holding L ~ U{1024..4096}
+    positions per sequence; cache rows beyond L are NaN.  Seeds 1000*6 + t as
+    for the named workloads.  `overrides` may shrink any size or give the
+    lengths L explicitly."""
+    p = dict(B=16, H=16, n_q=1, n_kv=4096, lo=1024, L=None)
+    p.update(overrides)
+    L = (int_uniform(_seed(6, 3), p["B"], min(p["lo"], p["n_kv"]), p["n_kv"]) if p["L"] is None
+         else np.asarray(p["L"], dtype=np.int32))
+    return make_sdpa(f"decode_bf16_{p['B']}x{p['H']}x{p['n_q']}q_cache{p['n_kv']}", "bf16", p["B"],
+                     p["H"], p["n_q"], p["n_kv"], 64, 64, 0.125, False, seqlens_kv=L, cfg_id=6)

@@ -28,8 +28,8 @@ STATUS = {0: "ATTN_OK", -1: "ATTN_E_INVALID", -2: "ATTN_E_UNSUPPORTED", -3: "ATT
           -4: "ATTN_E_WORKSPACE", -5: "ATTN_E_HIP"}
 
 # every entry point that include/attn_sdpa.h declares
-EXPORTS = ("attn_sdpa_fwd", "attn_mha_workspace_bytes", "attn_mha_fwd", "attn_linear_fwd",
-           "attn_status_str", "attn_abi_version")
+EXPORTS = ("attn_sdpa_fwd", "attn_mha_workspace_bytes", "attn_mha_fwd", "attn_decode_workspace_bytes",
+           "attn_decode_fwd", "attn_linear_fwd", "attn_status_str", "attn_abi_version")
 
 
 class AttnError(RuntimeError):
@@ -62,6 +62,11 @@ def lib() -> ctypes.CDLL:
         L.attn_mha_fwd.argtypes = [i, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp,
                                    ctypes.c_float, i, vp, vp, vp, ctypes.c_size_t, vp]
         L.attn_mha_fwd.restype = i
+        L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+        L.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_decode_fwd.argtypes = [i, i, i, i, i, i, i, vp, sp, vp, sp, vp, sp, vp, sp, ctypes.c_float,
+                                      vp, vp, vp, ctypes.c_size_t, vp]
+        L.attn_decode_fwd.restype = i
         L.attn_linear_fwd.argtypes = [i, i, i, i, vp, ctypes.c_int64, vp, vp, ctypes.c_int64, vp]
         L.attn_linear_fwd.restype = i
         L.attn_status_str.argtypes = [i]
@@ -185,6 +190,39 @@ def mha(x_q, x_kv, w_q, w_k, w_v, w_o, heads, scale=None, causal=False, seqlens_
                             _stream(stream))
     _check("attn_mha_fwd", rc)
     return out
+
+
+def decode_workspace_bytes(batch, heads, n_q, n_kv, d_k=64, d_v=64, dtype=ATTN_BF16) -> int:
+    return int(lib().attn_decode_workspace_bytes(dtype, batch, heads, n_q, n_kv, d_k, d_v))
+
+
+def decode(q, k_cache, v_cache, scale=None, seqlens_kv=None, return_lse=False, out=None,
+           workspace=None, stream=None):
+    """One decoding step over a key/value cache (bf16, head size 64): the n_q
+    (<= 32) queries of each sequence are its newest positions and attend to
+    the cache up to their own position.  q [B,H,n_q,64], k_cache/v_cache
+    [B,H,n_kv,64] (any strides with a contiguous last dimension), seqlens_kv
+    int32 [B] cache lengths (None = n_kv).  Returns o (and lse)."""
+    torch = _torch()
+    B, H, n_q, d_k = q.shape
+    n_kv, d_v = k_cache.shape[2], v_cache.shape[3]
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, H, n_q, d_v), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device) if return_lse else None
+    nbytes = decode_workspace_bytes(B, H, max(n_q, 1), n_kv, d_k, d_v, dt)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    sq, sk, sv, so = (_strides4(t) for t in (q, k_cache, v_cache, out))
+    rc = lib().attn_decode_fwd(dt, B, H, n_q, n_kv, d_k, d_v,
+                               q.data_ptr() or None, ctypes.byref(sq), k_cache.data_ptr() or None,
+                               ctypes.byref(sk), v_cache.data_ptr() or None, ctypes.byref(sv),
+                               out.data_ptr() or None, ctypes.byref(so),
+                               0.0 if scale is None else float(scale), _lens_ptr(seqlens_kv, B, q.device),
+                               None if lse is None else lse.data_ptr(), workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("attn_decode_fwd", rc)
+    return (out, lse) if return_lse else out
 
 
 def linear(x, w, out=None, stream=None):

@@ -13,6 +13,7 @@
 namespace {
 
 using attn::GemmBf16Params;
+using attn::SdpaDecodeParams;
 using attn::SdpaBf16Params;
 using attn::SdpaF32Params;
 
@@ -121,6 +122,41 @@ int launch_sdpa(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k,
   p.scale = scale;
   p.causal = mask == ATTN_MASK_CAUSAL;
   return hip_status(attn::launch_sdpa_f32(p, stream));
+}
+
+// Workspace of the decoding step: fp32 partial O [B*H][chunks][n_q][64], then
+// (m, l) pairs [B*H][chunks][n_q][2], each region 256-byte aligned.
+struct DecodeLayout {
+  int chunk_tiles, n_chunks;
+  size_t ml_off, total_bytes;
+};
+
+size_t round256(size_t x);
+
+DecodeLayout decode_layout(int batch, int heads, int n_q, int n_kv) {
+  DecodeLayout L;
+  attn::sdpa_decode_plan(batch, heads, n_kv, &L.chunk_tiles, &L.n_chunks);
+  const size_t rows = (size_t)batch * heads * L.n_chunks * n_q;
+  L.ml_off = round256(rows * 64 * sizeof(float));
+  L.total_bytes = L.ml_off + round256(rows * 2 * sizeof(float));
+  return L;
+}
+
+// Decoding-step sizes: bf16, head size 64, 1 <= n_q <= 32, grids in range.
+bool decode_sizes_ok(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k, int d_v, int* err) {
+  if (dt != ATTN_F32 && dt != ATTN_BF16) { *err = ATTN_E_INVALID; return false; }
+  if (batch < 1 || heads < 1 || n_q < 1 || n_kv < 0 || d_k < 1 || d_v < 1) {
+    *err = ATTN_E_INVALID;
+    return false;
+  }
+  if (dt != ATTN_BF16 || d_k != 64 || d_v != 64 || n_q > 32) { *err = ATTN_E_UNSUPPORTED; return false; }
+  int ct, nc;
+  attn::sdpa_decode_plan(batch, heads, n_kv, &ct, &nc);
+  if ((int64_t)batch * heads * nc > kMaxGrid || (int64_t)batch * heads * n_q > kMaxGrid) {
+    *err = ATTN_E_UNSUPPORTED;
+    return false;
+  }
+  return true;
 }
 
 // Workspace regions of the MHA block (bf16 elements), each 256-byte aligned.
@@ -302,6 +338,47 @@ int attn_linear_fwd(attn_dtype dt, int m, int k, int n, const void* x, int64_t l
   g.c = static_cast<uint16_t*>(y);
   g.lda = ldx; g.ldc = ldy; g.M = m; g.N = n; g.K = k; g.n_panel = n;
   return hip_status(attn::launch_gemm_bf16(g, static_cast<hipStream_t>(stream_)));
+}
+
+size_t attn_decode_workspace_bytes(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k,
+                                   int d_v) {
+  int err;
+  if (!decode_sizes_ok(dt, batch, heads, n_q, n_kv, d_k, d_v, &err)) return 0;
+  return decode_layout(batch, heads, n_q, n_kv).total_bytes;
+}
+
+int attn_decode_fwd(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k, int d_v,
+                    const void* q, const attn_strides* sq, const void* k, const attn_strides* sk,
+                    const void* v, const attn_strides* sv, void* o, const attn_strides* so, float scale,
+                    const int32_t* seqlens_kv, float* lse, void* workspace, size_t workspace_bytes,
+                    attn_stream_t stream) {
+  if (n_q == 0 && dt == ATTN_BF16 && batch >= 1 && heads >= 1 && n_kv >= 0) return ATTN_OK;
+  int err = ATTN_OK;
+  if (!decode_sizes_ok(dt, batch, heads, n_q, n_kv, d_k, d_v, &err)) return err;
+  attn_strides st[4];
+  const int rc = check_sdpa(dt, batch, heads, n_q, n_kv, d_k, d_v, q, sq, k, sk, v, sv, o, so, &scale,
+                            ATTN_MASK_NONE, lse, st);
+  if (rc != ATTN_OK) return rc;
+  const DecodeLayout L = decode_layout(batch, heads, n_q, n_kv);
+  if (!workspace || workspace_bytes < L.total_bytes) return ATTN_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return ATTN_E_ALIGN;
+  SdpaDecodeParams p = {};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.seqlens_kv = seqlens_kv;
+  p.qs_b = st[0].b; p.qs_h = st[0].h; p.qs_n = st[0].n;
+  p.ks_b = st[1].b; p.ks_h = st[1].h; p.ks_n = st[1].n;
+  p.vs_b = st[2].b; p.vs_h = st[2].h; p.vs_n = st[2].n;
+  p.os_b = st[3].b; p.os_h = st[3].h; p.os_n = st[3].n;
+  p.batch = batch; p.heads = heads; p.n_q = n_q; p.n_kv = n_kv;
+  p.chunk_tiles = L.chunk_tiles; p.n_chunks = L.n_chunks;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.part_o = static_cast<float*>(workspace);
+  p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.ml_off);
+  return hip_status(attn::launch_sdpa_decode_bf16(p, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

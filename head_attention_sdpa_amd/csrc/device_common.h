@@ -98,5 +98,13 @@ __device__ __forceinline__ float sum_with_partner(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Attention K/V tile layout in LDS: 64 rows x 128 B, no padding; the 16-byte
+// chunk c of row r is stored at chunk position c ^ swz(r), so that the lane
+// patterns of the two readers hit distinct banks:
+//   K (rows of 16 consecutive keys, one chunk each):  swz = (r >> 1) & 7
+//   V (transposed reads of 4 rows x 2 or 4 chunks):    swz = ((r >> 1) & 1) << 2
+__device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz_v(int r) { return ((r >> 1) & 1) << 2; }
+
 }  // namespace
 }  // namespace attn

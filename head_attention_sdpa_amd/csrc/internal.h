@@ -25,6 +25,32 @@ struct SdpaBf16Params {
   int causal;
 };
 
+// One decoding step over a key/value cache, bf16, head size 64: the n_q
+// (<= 32) queries are the newest positions L_kv - n_q + i of each sequence.
+// Keys are split into chunks of chunk_tiles * 64; each chunk leaves its
+// unnormalised partial result in the workspace, and a second kernel merges
+// the chunks.
+struct SdpaDecodeParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;                   // [batch*heads*n_q] or null
+  const int32_t* seqlens_kv;    // [batch] or null (= n_kv)
+  int64_t qs_b, qs_h, qs_n;
+  int64_t ks_b, ks_h, ks_n;
+  int64_t vs_b, vs_h, vs_n;
+  int64_t os_b, os_h, os_n;
+  int batch, heads, n_q, n_kv;
+  int chunk_tiles, n_chunks;    // key tiles per chunk; chunks per (b, h)
+  float scale_log2;
+  float* part_o;                // [batch*heads][n_chunks][n_q][64]: sum_j 2^(s_j - m) V_j
+  float* part_ml;               // [batch*heads][n_chunks][n_q][2]: shift m (log2 units), sum l
+};
+
+// Chunking of the decoding step for these sizes (the workspace depends on it).
+void sdpa_decode_plan(int batch, int heads, int n_kv, int* chunk_tiles, int* n_chunks);
+
 // Scaled dot-product attention, fp32 storage and arithmetic, head sizes <= 64.
 struct SdpaF32Params {
   const float* q;
@@ -59,6 +85,7 @@ struct GemmBf16Params {
 // the caller (abi.cpp) before these are reached.
 hipError_t launch_sdpa_bf16(const SdpaBf16Params& p, hipStream_t stream);
 hipError_t launch_sdpa_f32(const SdpaF32Params& p, hipStream_t stream);
+hipError_t launch_sdpa_decode_bf16(const SdpaDecodeParams& p, hipStream_t stream);
 hipError_t launch_gemm_bf16(const GemmBf16Params& p, hipStream_t stream);
 bool gemm_bf16_main_supported(const GemmBf16Params& p);   // shapes the fast kernel takes
 

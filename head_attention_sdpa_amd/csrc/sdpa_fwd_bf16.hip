@@ -56,13 +56,6 @@ __device__ __forceinline__ void map_block(int bid, int bh_total, int nqb, int ca
   qb = causal ? nqb - 1 - qb_idx : qb_idx;
 }
 
-// LDS tile layout: 64 rows x 128 B, no padding; the 16-byte chunk c of row r
-// is stored at chunk position c ^ swz(r), so that the lane patterns of the
-// two readers hit distinct banks:
-//   K (rows of 16 consecutive keys, one chunk each):  swz = (r >> 1) & 7
-//   V (transposed reads of 4 rows x 2 or 4 chunks):    swz = ((r >> 1) & 1) << 2
-__device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int swz_v(int r) { return ((r >> 1) & 1) << 2; }
 
 
 // One workgroup = (batch, head, 32*NW queries); wave w owns queries

@@ -14,6 +14,11 @@
  *                  Self-attention passes x_kv == x_q; encoder-decoder
  *                  attention passes the encoder output as x_kv (section 3.2.3;
  *                  rockcohen.cc 5.3).
+ *   attn_decode_fwd one decoding step over a key/value cache: the newest
+ *                  queries of each sequence attend to the cached keys up to
+ *                  their own position (autoregressive generation, section
+ *                  3.2.3; attention-paper-guide sections 05 and 07+; the csdn
+ *                  blog, section 3.6).
  *   attn_linear_fwd one projection of that block on its own, Y = X.W (the
  *                  products X W_i^Q, X W_i^K, X W_i^V and Concat(...) W^O of
  *                  section 3.2.2; rockcohen.cc 5.2).
@@ -49,7 +54,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 typedef void* attn_stream_t; /* hipStream_t */
 
@@ -139,6 +144,46 @@ int attn_mha_fwd(attn_dtype dt, int batch, int n_q, int n_kv, int d_model, int h
 
 /* Human-readable name of an attn_status value (static storage). */
 const char* attn_status_str(int status);
+
+/*
+ * attn_decode_workspace_bytes -- workspace that attn_decode_fwd needs for
+ * these sizes (fp32 partial results of the key chunks), or 0 if the sizes
+ * are invalid or unsupported.
+ */
+size_t attn_decode_workspace_bytes(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k,
+                                   int d_v);
+
+/*
+ * attn_decode_fwd -- one decoding step over a key/value cache.
+ *
+ * The n_q queries of sequence b are its newest positions: query i sits at
+ * position P = L_kv[b] - n_q + i, where L_kv[b] = seqlens_kv[b] (clamped to
+ * [0, n_kv]) or n_kv, and attends to the cached keys j <= P (the decoder's
+ * causal mask, aligned at the end of the cache).  Cache rows j >= L_kv[b] are
+ * never used and may hold anything.  A query with P < 0 has no legal key:
+ * its row of o is zeros and its lse -inf.  n_q = 1 is plain attention of the
+ * new token over the first L_kv[b] keys.
+ *
+ *   q  [batch, heads, n_q, 64]     o   [batch, heads, n_q, 64]
+ *   k  [batch, heads, n_kv, 64]    lse [batch, heads, n_q] fp32 or NULL
+ *   v  [batch, heads, n_kv, 64]        (natural log of the softmax denominator)
+ *   dt          ATTN_BF16 only (ATTN_F32 gives ATTN_E_UNSUPPORTED); d_k = d_v = 64.
+ *   1 <= n_q <= 32 (n_q = 0 does nothing), n_kv >= 0 (the cache capacity).
+ *   sq, sk, sv, so, scale: as in attn_sdpa_fwd (strides NULL = contiguous,
+ *               16-byte alignment, row strides >= 64 elements).
+ *   seqlens_kv  device int32 [batch] (cache lengths including the n_q new
+ *               positions) or NULL.
+ *   workspace   device memory of at least attn_decode_workspace_bytes(...)
+ *               bytes, 256-byte aligned; contents on entry are ignored.
+ * The keys are processed in chunks of whole 64-key tiles by independent
+ * workgroups, and a second kernel merges the chunks.  o must not alias q, k,
+ * v or the workspace.  Returns ATTN_OK or a negative attn_status.
+ */
+int attn_decode_fwd(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k, int d_v,
+                    const void* q, const attn_strides* sq, const void* k, const attn_strides* sk,
+                    const void* v, const attn_strides* sv, void* o, const attn_strides* so, float scale,
+                    const int32_t* seqlens_kv, float* lse, void* workspace, size_t workspace_bytes,
+                    attn_stream_t stream);
 
 /*
  * attn_linear_fwd -- y = x . w, no bias (one projection of the multi-head

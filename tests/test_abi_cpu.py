@@ -134,3 +134,41 @@ def linear_call(dt=1, m=64, k=128, n=256, x=FAKE, ldx=128, w=FAKE, y=FAKE, ldy=2
 ])
 def test_linear_validation(kw, code):
     assert linear_call(**kw) == code
+
+
+def decode_call(dt=1, B=2, H=2, nq=1, nkv=100, dk=64, dv=64, q=FAKE, k=FAKE, v=FAKE, o=FAKE,
+                ws=FAKE, wsb=1 << 30, scale=0.0):
+    return attn.lib().attn_decode_fwd(dt, B, H, nq, nkv, dk, dv, q, None, k, None, v, None, o, None,
+                                      scale, None, None, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), -1),
+    (dict(B=0), -1),
+    (dict(nkv=-1), -1),
+    (dict(q=None), -1),
+    (dict(k=None), -1),
+    (dict(scale=-1.0), -1),
+    (dict(dt=0), -2),
+    (dict(nq=33), -2),
+    (dict(dk=32), -2),
+    (dict(q=MISALIGNED), -3),
+    (dict(ws=FAKE + 64), -3),
+    (dict(ws=None), -4),
+    (dict(wsb=64), -4),
+    (dict(nq=0, q=None, o=None), 0),   # nothing to do: no launch
+])
+def test_decode_validation(kw, code):
+    assert decode_call(**kw) == code
+
+
+def test_decode_workspace_bytes():
+    L = attn.lib()
+    # 16 x 16 heads, one query, 4096-key cache: 8 chunks of 8 tiles per (b, h);
+    # fp32 partial O (64 per row) and (m, l) per (b, h, chunk, query)
+    rows = 16 * 16 * 8 * 1
+    assert L.attn_decode_workspace_bytes(1, 16, 16, 1, 4096, 64, 64) == rows * 64 * 4 + rows * 2 * 4
+    assert L.attn_decode_workspace_bytes(0, 16, 16, 1, 4096, 64, 64) == 0   # f32 unsupported
+    assert L.attn_decode_workspace_bytes(1, 16, 16, 33, 4096, 64, 64) == 0  # n_q > 32
+    assert L.attn_decode_workspace_bytes(1, 16, 16, 1, 4096, 32, 32) == 0
+    assert L.attn_decode_workspace_bytes(1, 1, 1, 1, 0, 64, 64) > 0         # empty cache: one chunk
