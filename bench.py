@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the attention forward hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decoder|encoder|cross|block]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decoder|encoder|cross|block|decode]
 
 A step is one pass of the hot path over one batch of synthetic input that is
 already resident in HBM:
@@ -10,6 +10,8 @@ already resident in HBM:
   cross              [16, 16, 256 q, 320 kv, 64], key lengths U{160..320}
   block              multi-head block, X [4, 4096, 1024], h = 16, causal:
                      QKV GEMM -> SDPA -> W^O GEMM
+  decode             one decoding step over a key/value cache: 16 x 16 heads,
+                     one new query each, cache 4096 with lengths U{1024..4096}
 Inputs rotate over enough copies to exceed the 256 MB Infinity Cache (cold
 cache), the K timed steps are captured once in a HIP graph and replayed, and
 HIP events on the launch stream bracket the replay.  Rank 0 prints one JSON
@@ -36,7 +38,7 @@ METRIC = "attention fwd TFLOP/s (bf16) + % of MFMA peak, h=8 d_k=64 n=256 causal
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 CACHE_BYTES = 256 << 20       # Infinity Cache
-WORKLOAD_CFG = {"encoder": 2, "decoder": 3, "cross": 4, "block": 5}
+WORKLOAD_CFG = {"encoder": 2, "decoder": 3, "cross": 4, "block": 5, "decode": 6}
 
 
 def legal_pairs(n_q, n_kv, causal, lq=None, lkv=None, batch=1):
@@ -292,10 +294,72 @@ def bench_block(K, W, args):
     return result, inp, flops
 
 
+def bench_decode(K, W, args):
+    """One decoding step over a key/value cache: 16 x 16 heads, one new query
+    per sequence, cache capacity 4096 with lengths U{1024..4096}.  HBM-bound:
+    the algorithmic bytes are the valid cache rows of K and V, Q and O."""
+    import ctypes
+    import torch
+    import attn_inputs as gen
+    import head_attention_sdpa_amd as attn
+
+    L = attn.lib()
+    dev = torch.device("cuda:0")
+    inp = gen.decode_workload()
+    B, H, n_q, n_kv, d_k, d_v = inp.shape
+    per_set = sum(a.nbytes for a in (inp.q_st, inp.k_st, inp.v_st)) + B * H * n_q * d_v * 2
+    R = max(1, math.ceil(2 * CACHE_BYTES / per_set)) if not args.hot else 1
+    base = [to_dev(a, "bf16", dev) for a in (inp.q_st, inp.k_st, inp.v_st)]
+    sets = [[t.clone() for t in base] for _ in range(R)]
+    outs = [torch.empty((B, H, n_q, d_v), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    lkv = torch.from_numpy(inp.seqlens_kv).to(dev)
+    nbytes = attn.decode_workspace_bytes(B, H, n_q, n_kv)
+    work = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+    def launch(s):
+        r = s % R
+        q, k, v = sets[r]
+        rc = L.attn_decode_fwd(attn.ATTN_BF16, B, H, n_q, n_kv, d_k, d_v, q.data_ptr(), None,
+                               k.data_ptr(), None, v.data_ptr(), None, outs[r].data_ptr(), None,
+                               float(inp.scale), lkv.data_ptr(), None, work.data_ptr(), nbytes,
+                               torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"attn_decode_fwd failed: {attn.status_str(rc)}")
+
+    ms, _ = time_graph(launch, K, W, torch)
+    Lk = inp.seqlens_kv.astype(np.int64)
+    pairs = int(H * sum(sum(max(0, min(int(l), int(l) - n_q + i + 1)) for i in range(n_q)) for l in Lk))
+    flops = pairs * 2 * (d_k + d_v)
+    algo_bytes = int(H * 2 * (B * n_q * (d_k + d_v) + int(Lk.sum()) * (d_k + d_v)))
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = algo_bytes / (ms * 1e-3) / 1e9
+    result = {
+        "value": tflops, "ms_per_step": ms, "pct_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "config": {"workload": inp.name, "batch": B, "heads": H, "n_q": n_q, "cache_capacity": n_kv,
+                   "cache_lengths": f"U{{1024..4096}}, sum {int(Lk.sum())}", "d_k": d_k,
+                   "cache": f"{'hot' if args.hot else 'cold'}: {R} rotating input sets of {per_set / 1e6:.1f} MB",
+                   "timing": "HIP graph of the timed steps, HIP events on the launch stream",
+                   "flops_per_step": flops, "algorithmic_bytes_per_step": algo_bytes},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": read_traffic("decode"),
+                     "kernel": "sdpa_decode_partial_bf16 + sdpa_decode_combine",
+                     "algorithmic_bytes_per_launch": algo_bytes},
+    }
+    return result, inp, flops
+
+
 def cpu_baseline(cfg_id, inp, flops_full):
     """The oracle as it stands, on the host cores, on a bounded sample."""
     import oracle
     threads = oracle.default_threads()
+    if cfg_id == 6:
+        best = float("inf")
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.decode(inp.q, inp.k, inp.v, scale=inp.scale, seqlens_kv=inp.seqlens_kv, nthreads=threads)
+            best = min(best, time.perf_counter() - t0)
+        return {"value": flops_full / best / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                "sample": "the full decoding step, best of 3", "seconds": best}
     if cfg_id == 5:
         # sample: batch element 0 of the block (a quarter of the workload)
         x = inp.x[:1]
@@ -360,6 +424,8 @@ def main():
     K, W = args.steps, args.warmup
     if cfg_id == 5:
         res, inp, flops = bench_block(K, W, args)
+    elif cfg_id == 6:
+        res, inp, flops = bench_decode(K, W, args)
     else:
         res, inp, flops = bench_sdpa(cfg_id, K, W, args)
     out = {"metric": METRIC, "value": res["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": K,

@@ -11,7 +11,7 @@
 //
 //   sdpa_decode_partial_bf16  workgroup = (batch*head, chunk), one wave; the
 //     wave's 32 lane columns are the (up to 32) queries.  K/V tiles of 64 keys
-//     stream through an NS-stage LDS-DMA ring -- a single wave needs no
+//     stream through an LDS-DMA ring -- a single wave needs no
 //     barrier, only its own vmcnt waits -- and each tile runs the same
 //     transposed MFMA products and online softmax as the prefill kernel.  The
 //     chunk leaves sum_j 2^(s_j - m) V_j, its shift m (log2 units) and sum l.
@@ -34,7 +34,11 @@ constexpr int D = 64;         // head size (d_k = d_v)
 constexpr int BN = 64;        // keys per tile
 constexpr int TILE_E = BN * D;
 constexpr float LN2 = 0.69314718055994530942f;
-constexpr int kTargetGroups = 2048;  // chunks x (b, h) to aim for: eight single waves per CU
+// Chunks x (b, h) to aim for, and the ring depth.  Measured on MI355X: a
+// two-stage ring (32 KiB, five single-wave workgroups per CU) streams the
+// cache faster than deeper rings with fewer workgroups per CU.
+constexpr int kTargetGroups = 2048;
+constexpr int kStages = 2;
 
 template <int NS>
 __global__ __launch_bounds__(64) void sdpa_decode_partial_bf16(const SdpaDecodeParams p) {
@@ -267,7 +271,8 @@ void sdpa_decode_plan(int batch, int heads, int n_kv, int* chunk_tiles, int* n_c
 hipError_t launch_sdpa_decode_bf16(const SdpaDecodeParams& p, hipStream_t stream) {
   const int64_t bh = (int64_t)p.batch * p.heads;
   if (bh == 0 || p.n_q == 0) return hipSuccess;
-  hipLaunchKernelGGL(sdpa_decode_partial_bf16<4>, dim3((unsigned)(bh * p.n_chunks)), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL(sdpa_decode_partial_bf16<kStages>, dim3((unsigned)(bh * p.n_chunks)), dim3(64), 0, stream,
+                     p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(sdpa_decode_combine, dim3((unsigned)(bh * p.n_q)), dim3(64), 0, stream, p);
