@@ -56,12 +56,13 @@ def _load():
                                        _I, _I, i, i]
         lib.oracle_mha_rows_f64.argtypes = [i, i, i, i, i, i, i, _D, _D, _D, _D, _D, _D, _L,
                                             ctypes.c_int64, _D, d, i, _I, _I, i, i]
+        lib.oracle_sdpa_window_f64.argtypes = [i, i, i, i, i, i, _D, _D, _D, _D, _D, d, i, _I, _I, i, i]
         lib.oracle_decode_f64.argtypes = [i, i, i, i, i, i, _D, _D, _D, _D, _D, d, _I, i]
         lib.oracle_linear_f64.argtypes = [i, i, i, _D, ctypes.c_int64, _L, ctypes.c_int64, _D, _D, i]
         lib.oracle_round_bf16.argtypes = [d]
         lib.oracle_round_bf16.restype = d
         for f in ("oracle_sdpa_f64", "oracle_sdpa_rows_f64", "oracle_mha_f64", "oracle_mha_rows_f64",
-                  "oracle_linear_f64", "oracle_decode_f64"):
+                  "oracle_linear_f64", "oracle_decode_f64", "oracle_sdpa_window_f64"):
             getattr(lib, f).restype = i
         _lib = lib
     return _lib
@@ -98,13 +99,15 @@ def _check(rc: int, what: str):
         raise MemoryError(f"{what}: out of memory")
 
 
-def sdpa(q, k, v, scale=None, causal=False, seqlens_q=None, seqlens_kv=None, nthreads=None):
+def sdpa(q, k, v, scale=None, causal=False, seqlens_q=None, seqlens_kv=None, window=None,
+         nthreads=None):
     """Scaled dot-product attention in fp64.
 
     q [B,H,n_q,d_k], k [B,H,n_kv,d_k], v [B,H,n_kv,d_v] (any float dtype; values
-    are taken exactly).  scale None means 1/sqrt(d_k).  Returns (o, lse) with
-    o [B,H,n_q,d_v] and lse [B,H,n_q] (natural log of the softmax denominator
-    including the max shift; -inf for rows without a legal key)."""
+    are taken exactly).  scale None means 1/sqrt(d_k).  window r (optional):
+    restricted attention, only keys with |i - j| <= r are legal.  Returns
+    (o, lse) with o [B,H,n_q,d_v] and lse [B,H,n_q] (natural log of the softmax
+    denominator including the max shift; -inf for rows without a legal key)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, n_q, d_k = q.shape
     n_kv, d_v = k.shape[2], v.shape[3]
@@ -115,10 +118,15 @@ def sdpa(q, k, v, scale=None, causal=False, seqlens_q=None, seqlens_kv=None, nth
     lse = np.empty((B, H, n_q))
     lq, plq = _lens(seqlens_q, B)
     lk, plk = _lens(seqlens_kv, B)
-    rc = _load().oracle_sdpa_f64(B, H, n_q, n_kv, d_k, d_v, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
-                                 _ptr(lse), scale, int(bool(causal)), plq, plk,
-                                 nthreads or default_threads())
-    _check(rc, "oracle_sdpa_f64")
+    if window is None:
+        rc = _load().oracle_sdpa_f64(B, H, n_q, n_kv, d_k, d_v, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                     _ptr(lse), scale, int(bool(causal)), plq, plk,
+                                     nthreads or default_threads())
+    else:
+        rc = _load().oracle_sdpa_window_f64(B, H, n_q, n_kv, d_k, d_v, _ptr(q), _ptr(k), _ptr(v),
+                                            _ptr(o), _ptr(lse), scale, int(bool(causal)), plq, plk,
+                                            int(window), nthreads or default_threads())
+    _check(rc, "oracle_sdpa")
     return o, lse
 
 

@@ -13,7 +13,8 @@
  *       vlmlib.cn summary and rockcohen.cc section 5.2), and
  *   (3) one projection of that block, y = x . W (no bias), and
  *   (4) one decoding step over a key/value cache (the newest n_q positions of
- *       each sequence under the causal mask).
+ *       each sequence under the causal mask), and
+ *   (5) restricted self-attention over a neighbourhood of radius r.
  *
  * Definitions followed literally, one query row at a time:
  *   legal(j)  <=>  j < n_kv  and  (no key lengths or j < L_kv[b])
@@ -64,12 +65,12 @@ static double round_bf16(double x) {
 
 /* ---- one query row of SDPA ---------------------------------------------- */
 /* q: d_k values; key j's row at K + j*k_stride, value j's row at V + j*v_stride.
- * legal_end: keys 0..legal_end-1 pass the length test; causal_i >= 0 adds the
- * causal test j <= causal_i.  s: scratch of n_kv doubles. */
+ * Keys legal_begin..legal_end-1 pass the length and window tests; causal_i >= 0
+ * adds the causal test j <= causal_i.  s: scratch of n_kv doubles. */
 static void sdpa_row(const double* q, const double* K, int64_t k_stride, const double* V,
-                     int64_t v_stride, int n_kv, int d_k, int d_v, double scale, int legal_end,
-                     int causal_i, double* s, double* out, double* lse) {
-#define LEGAL(j) ((j) < legal_end && (causal_i < 0 || (j) <= causal_i))
+                     int64_t v_stride, int n_kv, int d_k, int d_v, double scale, int legal_begin,
+                     int legal_end, int causal_i, double* s, double* out, double* lse) {
+#define LEGAL(j) ((j) >= legal_begin && (j) < legal_end && (causal_i < 0 || (j) <= causal_i))
   int any = 0;
   double m = -INFINITY;
   for (int j = 0; j < n_kv; ++j) {              /* scores of the legal keys, and their max */
@@ -149,6 +150,7 @@ typedef struct {
   const int *seqlens_q, *seqlens_kv;
   const int64_t* rows;   /* NULL: row r is flat index r; else rows[r] is the flat index */
   int decode;            /* 1: query i is sequence position L_kv[b] - n_q + i (see below) */
+  int window;            /* >= 0: only keys with |i - j| <= window are legal */
 } sdpa_ctx;
 
 static void sdpa_range(void* p, int64_t begin, int64_t end, double* s) {
@@ -176,7 +178,12 @@ static void sdpa_range(void* p, int64_t begin, int64_t end, double* s) {
       if (pos < 0) legal_end = 0;                     /* before the sequence: no legal key */
       else causal_i = pos;
     }
-    sdpa_row(q, K, c->d_k, V, c->d_v, c->n_kv, c->d_k, c->d_v, c->scale, legal_end,
+    int legal_begin = 0;
+    if (c->window >= 0) {                             /* restricted: the neighbourhood |i - j| <= r */
+      legal_begin = i - c->window;
+      if (i + c->window + 1 < legal_end) legal_end = i + c->window + 1;
+    }
+    sdpa_row(q, K, c->d_k, V, c->d_v, c->n_kv, c->d_k, c->d_v, c->scale, legal_begin, legal_end,
              causal_i, s, out, lse);
   }
 }
@@ -194,7 +201,25 @@ int oracle_sdpa_f64(int B, int H, int n_q, int n_kv, int d_k, int d_v, const dou
                     int causal, const int* seqlens_q, const int* seqlens_kv, int nthreads) {
   if (B < 0 || H < 0 || n_q < 0 || n_kv < 0 || d_k < 1 || d_v < 1 || !(scale > 0.0)) return ORACLE_EINVAL;
   if (!check_lengths(seqlens_q, B, n_q) || !check_lengths(seqlens_kv, B, n_kv)) return ORACLE_EINVAL;
-  sdpa_ctx c = {B, H, n_q, n_kv, d_k, d_v, scale, causal, q, k, v, o, lse, seqlens_q, seqlens_kv, NULL, 0};
+  sdpa_ctx c = {B, H, n_q, n_kv, d_k, d_v, scale, causal, q, k, v, o, lse, seqlens_q, seqlens_kv, NULL, 0, -1};
+  return parallel_for((int64_t)B * H * n_q, nthreads, n_kv > 0 ? n_kv : 1, sdpa_range, &c);
+}
+
+/* Restricted self-attention: query i only attends to the keys of its
+ * neighbourhood of radius r, |i - j| <= r (a window of 2r + 1 positions
+ * centred on i, cut at the sequence ends), on top of the length and causal
+ * tests -- the paper's proposal for very long inputs, cost O(r n d) instead of
+ * O(n^2 d) (section 4 and Table 1; the csdn blog, section 4.3; the vlmlib.cn
+ * summary's limitations paragraph). */
+int oracle_sdpa_window_f64(int B, int H, int n_q, int n_kv, int d_k, int d_v, const double* q,
+                           const double* k, const double* v, double* o, double* lse, double scale,
+                           int causal, const int* seqlens_q, const int* seqlens_kv, int window,
+                           int nthreads) {
+  if (B < 0 || H < 0 || n_q < 0 || n_kv < 0 || d_k < 1 || d_v < 1 || !(scale > 0.0) || window < 0)
+    return ORACLE_EINVAL;
+  if (!check_lengths(seqlens_q, B, n_q) || !check_lengths(seqlens_kv, B, n_kv)) return ORACLE_EINVAL;
+  sdpa_ctx c = {B, H, n_q, n_kv, d_k, d_v, scale, causal, q, k, v, o, lse, seqlens_q, seqlens_kv, NULL, 0,
+                window};
   return parallel_for((int64_t)B * H * n_q, nthreads, n_kv > 0 ? n_kv : 1, sdpa_range, &c);
 }
 
@@ -212,7 +237,7 @@ int oracle_decode_f64(int B, int H, int n_q, int n_kv, int d_k, int d_v, const d
                       const int* seqlens_kv, int nthreads) {
   if (B < 0 || H < 0 || n_q < 0 || n_kv < 0 || d_k < 1 || d_v < 1 || !(scale > 0.0)) return ORACLE_EINVAL;
   if (!check_lengths(seqlens_kv, B, n_kv)) return ORACLE_EINVAL;
-  sdpa_ctx c = {B, H, n_q, n_kv, d_k, d_v, scale, 0, q, k, v, o, lse, NULL, seqlens_kv, NULL, 1};
+  sdpa_ctx c = {B, H, n_q, n_kv, d_k, d_v, scale, 0, q, k, v, o, lse, NULL, seqlens_kv, NULL, 1, -1};
   return parallel_for((int64_t)B * H * n_q, nthreads, n_kv > 0 ? n_kv : 1, sdpa_range, &c);
 }
 
@@ -226,7 +251,7 @@ int oracle_sdpa_rows_f64(int B, int H, int n_q, int n_kv, int d_k, int d_v, cons
   if (!check_lengths(seqlens_q, B, n_q) || !check_lengths(seqlens_kv, B, n_kv)) return ORACLE_EINVAL;
   for (int64_t r = 0; r < nrows; ++r)
     if (rows[r] < 0 || rows[r] >= (int64_t)B * H * n_q) return ORACLE_EINVAL;
-  sdpa_ctx c = {B, H, n_q, n_kv, d_k, d_v, scale, causal, q, k, v, o, lse, seqlens_q, seqlens_kv, rows, 0};
+  sdpa_ctx c = {B, H, n_q, n_kv, d_k, d_v, scale, causal, q, k, v, o, lse, seqlens_q, seqlens_kv, rows, 0, -1};
   return parallel_for(nrows, nthreads, n_kv > 0 ? n_kv : 1, sdpa_range, &c);
 }
 
@@ -296,7 +321,7 @@ static void mha_attn_range(void* p, int64_t begin, int64_t end, double* s) {
       const double* q = c->qp + r * wq + (int64_t)h * c->d_k;
       const double* K = c->kp + kvb * c->n_kv * wq + (int64_t)h * c->d_k;
       const double* V = c->vp + kvb * c->n_kv * wv + (int64_t)h * c->d_v;
-      sdpa_row(q, K, wq, V, wv, c->n_kv, c->d_k, c->d_v, c->scale, legal_end,
+      sdpa_row(q, K, wq, V, wv, c->n_kv, c->d_k, c->d_v, c->scale, 0, legal_end,
                c->causal ? i : -1, s, ocat + (int64_t)h * c->d_v, NULL);
     }
     if (c->round_out) for (int64_t x = 0; x < wv; ++x) ocat[x] = round_bf16(ocat[x]);

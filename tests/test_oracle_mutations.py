@@ -33,6 +33,9 @@ MUTATIONS = {
                           "const double* vj = V + (int64_t)(j == 0 ? 0 : j - 1) * v_stride;"),
     "decode alignment off by one": ("int pos = legal_end - c->n_q + i;", "int pos = legal_end - c->n_q + i + 1;"),
     "decode aligned at the start": ("int pos = legal_end - c->n_q + i;", "int pos = i;"),
+    "window one short on the left": ("legal_begin = i - c->window;", "legal_begin = i - c->window + 1;"),
+    "window one long on the right": ("if (i + c->window + 1 < legal_end) legal_end = i + c->window + 1;",
+                                     "if (i + c->window + 2 < legal_end) legal_end = i + c->window + 2;"),
     "projection weight transposed": ("for (int n = 0; n < g->N; ++n) c[n] += ak * wk[n];",
                                      "for (int n = 0; n < g->N; ++n) c[n] += ak * g->w[(int64_t)n * g->K + kk];"),
 }

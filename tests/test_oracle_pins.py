@@ -418,3 +418,45 @@ def test_decode_per_sequence_lengths_and_short_sequences():
     assert np.all(o[2, :, 0] == 0.0) and np.all(lse[2, :, 0] == -np.inf)
     of, lf = oracle.sdpa(q[2:3, :, 1:], k[2:3, :, :2], v[2:3, :, :2], causal=True)
     assert np.array_equal(o[2, :, 1:], of[0]) and np.array_equal(lse[2, :, 1:], lf[0])
+
+
+# ---------------------------------------------------------------------------
+# Restricted self-attention over a neighbourhood of radius r (the paper's
+# proposal for very long inputs: the csdn blog section 4.3, the vlmlib.cn
+# summary's limitations paragraph; reading: key j is legal iff |i - j| <= r)
+# ---------------------------------------------------------------------------
+def test_window_wider_than_the_sequence_is_full_attention():
+    q, k, v = rnd(500, (2, 2, 19, 8)), rnd(501, (2, 2, 19, 8)), rnd(502, (2, 2, 19, 8))
+    for causal in (False, True):
+        full = oracle.sdpa(q, k, v, causal=causal)
+        win = oracle.sdpa(q, k, v, causal=causal, window=18)
+        assert np.array_equal(full[0], win[0]) and np.array_equal(full[1], win[1])
+
+
+def test_window_zero_attends_to_itself():
+    """r = 0 leaves the diagonal only: O[i] = V[i] exactly and lse = s_ii.
+    Catches an off-by-one on either side of the band."""
+    q, k, v = rnd(510, (1, 2, 9, 8)), rnd(511, (1, 2, 9, 8)), rnd(512, (1, 2, 9, 8))
+    o, lse = oracle.sdpa(q, k, v, window=0, scale=0.3)
+    assert np.array_equal(o, v)
+    assert np.allclose(lse, 0.3 * np.einsum("bhid,bhid->bhi", q, k), rtol=0, atol=1e-13)
+
+
+def test_window_equals_attention_over_the_neighbourhood():
+    """Masking outside the band equals attention of each query over the sliced
+    keys k[i-r .. i+r] (renormalising over the legal set, rockcohen.cc 6.3),
+    with and without the causal mask and with key lengths."""
+    B, H, n, d, r = 2, 2, 21, 8, 3
+    q, k, v = rnd(520, (B, H, n, d)), rnd(521, (B, H, n, d)), rnd(522, (B, H, n, d))
+    L = np.array([21, 12], np.int32)
+    for causal in (False, True):
+        o, lse = oracle.sdpa(q, k, v, causal=causal, window=r, seqlens_kv=L)
+        for b in range(B):
+            for i in range(n):
+                lo, hi = max(0, i - r), min(int(L[b]), (i if causal else i + r) + 1)
+                if hi <= lo:
+                    assert np.all(o[b, :, i] == 0) and np.all(lse[b, :, i] == -np.inf)
+                    continue
+                ref, rl = oracle.sdpa(q[b:b + 1, :, i:i + 1], k[b:b + 1, :, lo:hi], v[b:b + 1, :, lo:hi])
+                assert np.abs(o[b, :, i] - ref[0, :, 0]).max() < 1e-13
+                assert np.abs(lse[b, :, i] - rl[0, :, 0]).max() < 1e-13
