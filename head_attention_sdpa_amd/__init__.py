@@ -28,7 +28,7 @@ STATUS = {0: "ATTN_OK", -1: "ATTN_E_INVALID", -2: "ATTN_E_UNSUPPORTED", -3: "ATT
           -4: "ATTN_E_WORKSPACE", -5: "ATTN_E_HIP"}
 
 # every entry point that include/attn_sdpa.h declares
-EXPORTS = ("attn_sdpa_fwd", "attn_mha_workspace_bytes", "attn_mha_fwd", "attn_decode_workspace_bytes",
+EXPORTS = ("attn_sdpa_fwd", "attn_sdpa_window_fwd", "attn_mha_workspace_bytes", "attn_mha_fwd", "attn_decode_workspace_bytes",
            "attn_decode_fwd", "attn_linear_fwd", "attn_status_str", "attn_abi_version")
 
 
@@ -57,6 +57,9 @@ def lib() -> ctypes.CDLL:
         L.attn_sdpa_fwd.argtypes = [i, i, i, i, i, i, i, vp, sp, vp, sp, vp, sp, vp, sp,
                                     ctypes.c_float, i, vp, vp, vp, vp]
         L.attn_sdpa_fwd.restype = i
+        L.attn_sdpa_window_fwd.argtypes = [i, i, i, i, i, i, i, vp, sp, vp, sp, vp, sp, vp, sp,
+                                           ctypes.c_float, i, i, vp, vp, vp, vp]
+        L.attn_sdpa_window_fwd.restype = i
         L.attn_mha_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
         L.attn_mha_workspace_bytes.restype = ctypes.c_size_t
         L.attn_mha_fwd.argtypes = [i, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp,
@@ -126,8 +129,9 @@ def _stream(stream):
 
 
 def sdpa(q, k, v, scale=None, causal=False, seqlens_q=None, seqlens_kv=None, return_lse=False,
-         out=None, stream=None):
+         out=None, stream=None, window=None):
     """Scaled dot-product attention forward on the GPU (see module docstring).
+    window r (optional): restricted attention, only keys with |i - j| <= r.
     Returns o [B,H,n_q,d_v] (and lse [B,H,n_q] fp32 if return_lse)."""
     torch = _torch()
     B, H, n_q, d_k = q.shape
@@ -143,14 +147,17 @@ def sdpa(q, k, v, scale=None, causal=False, seqlens_q=None, seqlens_kv=None, ret
         out = torch.empty((B, H, n_q, d_v), dtype=q.dtype, device=q.device)
     lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device) if return_lse else None
     sq, sk, sv, so = _strides4(q), _strides4(k), _strides4(v), _strides4(out)
-    rc = lib().attn_sdpa_fwd(dt, B, H, n_q, n_kv, d_k, d_v,
-                             q.data_ptr(), ctypes.byref(sq), k.data_ptr(), ctypes.byref(sk),
-                             v.data_ptr(), ctypes.byref(sv), out.data_ptr(), ctypes.byref(so),
-                             0.0 if scale is None else float(scale),
-                             ATTN_MASK_CAUSAL if causal else ATTN_MASK_NONE,
-                             _lens_ptr(seqlens_q, B, q.device), _lens_ptr(seqlens_kv, B, q.device),
-                             None if lse is None else lse.data_ptr(), _stream(stream))
-    _check("attn_sdpa_fwd", rc)
+    common = (q.data_ptr(), ctypes.byref(sq), k.data_ptr(), ctypes.byref(sk),
+              v.data_ptr(), ctypes.byref(sv), out.data_ptr(), ctypes.byref(so),
+              0.0 if scale is None else float(scale), ATTN_MASK_CAUSAL if causal else ATTN_MASK_NONE)
+    tail = (_lens_ptr(seqlens_q, B, q.device), _lens_ptr(seqlens_kv, B, q.device),
+            None if lse is None else lse.data_ptr(), _stream(stream))
+    if window is None:
+        rc = lib().attn_sdpa_fwd(dt, B, H, n_q, n_kv, d_k, d_v, *common, *tail)
+        _check("attn_sdpa_fwd", rc)
+    else:
+        rc = lib().attn_sdpa_window_fwd(dt, B, H, n_q, n_kv, d_k, d_v, *common, int(window), *tail)
+        _check("attn_sdpa_window_fwd", rc)
     return (out, lse) if return_lse else out
 
 

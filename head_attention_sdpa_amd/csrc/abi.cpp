@@ -86,8 +86,8 @@ int check_sdpa(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k, 
 
 int launch_sdpa(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k, int d_v,
                 const void* q, const void* k, const void* v, void* o, const attn_strides st[4],
-                float scale, attn_mask mask, const int32_t* lq, const int32_t* lkv, float* lse,
-                hipStream_t stream) {
+                float scale, attn_mask mask, int window, const int32_t* lq, const int32_t* lkv,
+                float* lse, hipStream_t stream) {
   if (dt == ATTN_BF16) {
     SdpaBf16Params p = {};
     p.q = static_cast<const uint16_t*>(q);
@@ -104,6 +104,7 @@ int launch_sdpa(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k,
     p.batch = batch; p.heads = heads; p.n_q = n_q; p.n_kv = n_kv;
     p.scale_log2 = scale * 1.4426950408889634f;
     p.causal = mask == ATTN_MASK_CAUSAL;
+    p.window = window;
     return hip_status(attn::launch_sdpa_bf16(p, stream));
   }
   SdpaF32Params p = {};
@@ -121,6 +122,7 @@ int launch_sdpa(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k,
   p.batch = batch; p.heads = heads; p.n_q = n_q; p.n_kv = n_kv; p.d_k = d_k; p.d_v = d_v;
   p.scale = scale;
   p.causal = mask == ATTN_MASK_CAUSAL;
+  p.window = window;
   return hip_status(attn::launch_sdpa_f32(p, stream));
 }
 
@@ -223,7 +225,21 @@ int attn_sdpa_fwd(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_
   const int rc = check_sdpa(dt, batch, heads, n_q, n_kv, d_k, d_v, q, sq, k, sk, v, sv, o, so,
                             &scale, mask, lse, st);
   if (rc != ATTN_OK) return rc;
-  return launch_sdpa(dt, batch, heads, n_q, n_kv, d_k, d_v, q, k, v, o, st, scale, mask,
+  return launch_sdpa(dt, batch, heads, n_q, n_kv, d_k, d_v, q, k, v, o, st, scale, mask, -1,
+                     seqlens_q, seqlens_kv, lse, static_cast<hipStream_t>(stream));
+}
+
+int attn_sdpa_window_fwd(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k, int d_v,
+                         const void* q, const attn_strides* sq, const void* k, const attn_strides* sk,
+                         const void* v, const attn_strides* sv, void* o, const attn_strides* so,
+                         float scale, attn_mask mask, int window, const int32_t* seqlens_q,
+                         const int32_t* seqlens_kv, float* lse, attn_stream_t stream) {
+  if (window < 0) return ATTN_E_INVALID;
+  attn_strides st[4];
+  const int rc = check_sdpa(dt, batch, heads, n_q, n_kv, d_k, d_v, q, sq, k, sk, v, sv, o, so,
+                            &scale, mask, lse, st);
+  if (rc != ATTN_OK) return rc;
+  return launch_sdpa(dt, batch, heads, n_q, n_kv, d_k, d_v, q, k, v, o, st, scale, mask, window,
                      seqlens_q, seqlens_kv, lse, static_cast<hipStream_t>(stream));
 }
 
@@ -308,7 +324,7 @@ int attn_mha_fwd(attn_dtype dt, int batch, int n_q, int n_kv, int d_model, int h
   // 2. attention per head, reading the projections through strides and
   //    writing the concatenation [B, n_q, H, 64] directly
   st[3] = attn_strides{(int64_t)n_q * hd, 64, hd};
-  rc = launch_sdpa(ATTN_BF16, batch, heads, n_q, n_kv, 64, 64, qp, kp, vp, obuf, st, scale, mask,
+  rc = launch_sdpa(ATTN_BF16, batch, heads, n_q, n_kv, 64, 64, qp, kp, vp, obuf, st, scale, mask, -1,
                    seqlens_q, seqlens_kv, nullptr, stream);
   if (rc != ATTN_OK) return rc;
 

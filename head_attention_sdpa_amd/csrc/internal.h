@@ -23,6 +23,7 @@ struct SdpaBf16Params {
   int n_qblocks;                // ceil(n_q / queries per workgroup)
   float scale_log2;             // scale * log2(e): scores go straight to exp2
   int causal;
+  int window;                   // >= 0: only keys with |i - j| <= window (restricted attention)
 };
 
 // One decoding step over a key/value cache, bf16, head size 64: the n_q
@@ -67,6 +68,7 @@ struct SdpaF32Params {
   int batch, heads, n_q, n_kv, d_k, d_v;
   float scale;
   int causal;
+  int window;                   // >= 0: only keys with |i - j| <= window
 };
 
 // C[M, N] = A[M, K] . B[K, N], bf16 in, fp32 accumulate, bf16 out (RNE).

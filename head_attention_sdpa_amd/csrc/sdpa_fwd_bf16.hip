@@ -91,14 +91,24 @@ void sdpa_fwd_bf16_d64(const SdpaBf16Params p) {
   const int q0 = qb * BM;
   const int qw0 = q0 + wave * 32;
   const int qi = qw0 + i32;
-  int kv_end = Lkv, wkv_end = Lkv;
+  // keys this workgroup / this wave needs: [kv_begin, kv_end) and
+  // [wkv_begin, wkv_end) (queries >= Lq are zeros: need nothing)
+  constexpr int kFar = 1 << 30;
+  int kv_end = Lkv, wkv_end = Lkv, kv_begin = 0, wkv_begin = 0;
   if (p.causal) {
     kv_end = min(kv_end, min(q0 + BM, Lq));
     wkv_end = min(wkv_end, min(qw0 + 32, Lq));
   }
+  if (p.window >= 0) {  // restricted attention: keys |i - j| <= window
+    kv_begin = max(0, q0 - p.window);
+    wkv_begin = max(0, qw0 - p.window);
+    kv_end = min(kv_end, min(q0 + BM, Lq) + p.window);
+    wkv_end = min(wkv_end, min(qw0 + 32, Lq) + p.window);
+  }
   if (q0 >= Lq) kv_end = 0;
   if (qw0 >= Lq) wkv_end = 0;
-  const int nblk = (kv_end + BN - 1) / BN;
+  const int t_begin = kv_begin / BN;  // first key tile of the workgroup
+  const int nblk = max(0, (kv_end + BN - 1) / BN - t_begin);
 
   const __bf16* Qb = reinterpret_cast<const __bf16*>(p.q) + b * p.qs_b + h * p.qs_h;
   const __bf16* Kb = reinterpret_cast<const __bf16*>(p.k) + b * p.ks_b + h * p.ks_h;
@@ -118,7 +128,8 @@ void sdpa_fwd_bf16_d64(const SdpaBf16Params p) {
     const int chunk = (lane & 7) ^ (is_v ? swz_v(r) : swz_k(r));
     dma_off[i] = (uint32_t)(((int64_t)r * (is_v ? p.vs_n : p.ks_n) + chunk * 8) * 2);
   }
-  auto issue_tile = [&](int t) {
+  auto issue_tile = [&](int j) {  // the workgroup's j-th tile, key tile t_begin + j, into stage j % NS
+    const int t = t_begin + j;
     const int64_t k_adv = (int64_t)t * BN * p.ks_n, v_adv = (int64_t)t * BN * p.vs_n;
     const i32x4 rk = make_rsrc(Kb + k_adv, (uint32_t)max<int64_t>(0, (int64_t)k_bytes - 2 * k_adv));
     const i32x4 rv = make_rsrc(Vb + v_adv, (uint32_t)max<int64_t>(0, (int64_t)v_bytes - 2 * v_adv));
@@ -126,7 +137,7 @@ void sdpa_fwd_bf16_d64(const SdpaBf16Params p) {
     for (int i = 0; i < IPT; ++i) {
       const int u = wave * IPT + i;
       const bool is_v = u >= 8;
-      const __bf16* dst = smem + (t % NS) * 2 * TILE_E + (is_v ? TILE_E : 0) + (u & 7) * 512;
+      const __bf16* dst = smem + (j % NS) * 2 * TILE_E + (is_v ? TILE_E : 0) + (u & 7) * 512;
       dma16(dma_off[i], is_v ? rv : rk, lds_addr(dst));
     }
   };
@@ -176,8 +187,9 @@ void sdpa_fwd_bf16_d64(const SdpaBf16Params p) {
     wait_vmcnt_le<IPT>(min(NS - 2, nblk - 1 - blk) * IPT);
     barrier_lds();  // tile blk visible; every wave is done with tile blk-1
     if (blk + NS - 1 < nblk) issue_tile(blk + NS - 1);  // into the stage of tile blk-1
-    const int key0 = blk * BN;
-    if (key0 >= wkv_end) continue;  // wave-uniform: keys after this wave's queries
+    const int key0 = (t_begin + blk) * BN;
+    // wave-uniform: the tile holds no key this wave's queries may see
+    if (key0 >= wkv_end || key0 + BN <= wkv_begin) continue;
     const __bf16* Ks = smem + (blk % NS) * 2 * TILE_E;
     const __bf16* Vs = Ks + TILE_E;
     f32x16 sc0 = {}, sc1 = {};
@@ -189,14 +201,21 @@ void sdpa_fwd_bf16_d64(const SdpaBf16Params p) {
       sc0 = mfma32(ka, qf[d], sc0);
       sc1 = mfma32(kb, qf[d], sc1);
     }
-    if (key0 + BN > Lkv || (p.causal && key0 + BN - 1 > qw0)) {
-      const int lim = p.causal ? min(Lkv - 1, qi) : Lkv - 1;
+    // -inf for illegal keys, only on tiles that cross a bound of some lane of
+    // the wave (key length, diagonal, or the band |i - j| <= window): key
+    // key0 + pos is legal iff thr_lo <= pos <= thr, where the lane's register
+    // r holds pos = 8*(r/4) + 4*g + r%4 (+32 in sc1)
+    const int hi_w = min(Lkv - 1, min(p.causal ? qw0 : kFar, p.window >= 0 ? qw0 + p.window : kFar));
+    const int lo_w = p.window >= 0 ? qw0 + 31 - p.window : -kFar;
+    if (key0 + BN - 1 > hi_w || key0 < lo_w) {
+      const int lim = min(Lkv - 1, min(p.causal ? qi : kFar, p.window >= 0 ? qi + p.window : kFar));
       const int thr = lim - key0 - 4 * g;
+      const int thr_lo = (p.window >= 0 ? qi - p.window : -kFar) - key0 - 4 * g;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int pos = 8 * (r >> 2) + (r & 3);
-        if (pos > thr) sc0[r] = -INFINITY;
-        if (pos + 32 > thr) sc1[r] = -INFINITY;
+        if (pos > thr || pos < thr_lo) sc0[r] = -INFINITY;
+        if (pos + 32 > thr || pos + 32 < thr_lo) sc1[r] = -INFINITY;
       }
     }
     float mx = fmaxf(sc0[0], sc1[0]);
@@ -206,7 +225,9 @@ void sdpa_fwd_bf16_d64(const SdpaBf16Params p) {
     const bool grow = mx > m + 8.f;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       const float m_new = grow ? mx : m;
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      // lanes that keep their shift use alpha = 1: exp2(m - m) would be NaN
+      // for a lane with no legal key yet (m = -inf)
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;  // m = -inf: 0
       l *= alpha;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {

@@ -34,21 +34,25 @@ __global__ __launch_bounds__(64) void sdpa_fwd_f32_kernel(const SdpaF32Params p)
   float* orow = p.o + b * p.os_b + h * p.os_h + (int64_t)i * p.os_n;
   float* lse = p.lse ? p.lse + ((int64_t)b * p.heads + h) * p.n_q + i : nullptr;
 
-  int jend = (i < Lq) ? Lkv : 0;
+  int jbeg = 0, jend = (i < Lq) ? Lkv : 0;
   if (p.causal) jend = min(jend, i + 1);
+  if (p.window >= 0) {   // restricted attention: keys |i - j| <= window
+    jbeg = max(0, i - p.window);
+    jend = min(jend, i + p.window + 1);
+  }
 
   float q[DMAX], o[DMAX];
   const float* qrow = p.q + b * p.qs_b + h * p.qs_h + (int64_t)i * p.qs_n;
 #pragma unroll
   for (int c = 0; c < DMAX; ++c) {
-    q[c] = (c < p.d_k && jend > 0) ? qrow[c] : 0.f;
+    q[c] = (c < p.d_k && jend > jbeg) ? qrow[c] : 0.f;
     o[c] = 0.f;
   }
 
   const float* Kb = p.k + b * p.ks_b + h * p.ks_h;
   const float* Vb = p.v + b * p.vs_b + h * p.vs_h;
   float m = -INFINITY, l = 0.f;
-  for (int j = 0; j < jend; ++j) {
+  for (int j = jbeg; j < jend; ++j) {
     const float* krow = Kb + (int64_t)j * p.ks_n;
     float dot = 0.f;
 #pragma unroll

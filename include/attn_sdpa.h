@@ -14,6 +14,10 @@
  *                  Self-attention passes x_kv == x_q; encoder-decoder
  *                  attention passes the encoder output as x_kv (section 3.2.3;
  *                  rockcohen.cc 5.3).
+ *   attn_sdpa_window_fwd  restricted self-attention: each query attends only
+ *                  to the keys of its neighbourhood of radius r, |i - j| <= r
+ *                  (the paper's proposal for very long inputs, cost O(r n d):
+ *                  section 4 and Table 1; the csdn blog, section 4.3).
  *   attn_decode_fwd one decoding step over a key/value cache: the newest
  *                  queries of each sequence attend to the cached keys up to
  *                  their own position (autoregressive generation, section
@@ -54,7 +58,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 typedef void* attn_stream_t; /* hipStream_t */
 
@@ -107,6 +111,20 @@ int attn_sdpa_fwd(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_
                   const void* v, const attn_strides* sv, void* o, const attn_strides* so,
                   float scale, attn_mask mask, const int32_t* seqlens_q,
                   const int32_t* seqlens_kv, float* lse, attn_stream_t stream);
+
+/*
+ * attn_sdpa_window_fwd -- attn_sdpa_fwd restricted to a band: key j is legal
+ * for query i only if also |i - j| <= window (window >= 0; a neighbourhood of
+ * 2*window + 1 positions centred on i, cut at the sequence ends; with
+ * ATTN_MASK_CAUSAL the keys i - window .. i).  Every other argument and rule
+ * is as for attn_sdpa_fwd; key tiles outside every query's band are never
+ * read.  window < 0 gives ATTN_E_INVALID.
+ */
+int attn_sdpa_window_fwd(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k, int d_v,
+                         const void* q, const attn_strides* sq, const void* k, const attn_strides* sk,
+                         const void* v, const attn_strides* sv, void* o, const attn_strides* so,
+                         float scale, attn_mask mask, int window, const int32_t* seqlens_q,
+                         const int32_t* seqlens_kv, float* lse, attn_stream_t stream);
 
 /*
  * attn_mha_workspace_bytes -- workspace that attn_mha_fwd needs for these

@@ -172,3 +172,12 @@ def test_decode_workspace_bytes():
     assert L.attn_decode_workspace_bytes(1, 16, 16, 33, 4096, 64, 64) == 0  # n_q > 32
     assert L.attn_decode_workspace_bytes(1, 16, 16, 1, 4096, 32, 32) == 0
     assert L.attn_decode_workspace_bytes(1, 1, 1, 1, 0, 64, 64) > 0         # empty cache: one chunk
+
+
+def test_sdpa_window_validation():
+    L = attn.lib()
+    s = attn.attn_strides(64 * 128, 64 * 128, 64)
+    args = (1, 1, 1, 128, 128, 64, 64, FAKE, None, FAKE, None, FAKE, None, FAKE, None, 0.0, 0)
+    assert L.attn_sdpa_window_fwd(*args, -1, None, None, None, None) == -1          # negative radius
+    assert L.attn_sdpa_window_fwd(1, 1, 1, 128, 128, 32, 32, *args[7:], 4, None, None, None, None) == -2
+    assert L.attn_sdpa_window_fwd(*args[:7], MISALIGNED, *args[8:], 4, None, None, None, None) == -3
