@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the attention forward hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decoder|encoder|cross|block|decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload decoder|encoder|cross|block|decode|window]
 
 A step is one pass of the hot path over one batch of synthetic input that is
 already resident in HBM:
@@ -12,6 +13,8 @@ already resident in HBM:
                      QKV GEMM -> SDPA -> W^O GEMM
   decode             one decoding step over a key/value cache: 16 x 16 heads,
                      one new query each, cache 4096 with lengths U{1024..4096}
+  window             restricted self-attention, [4, 16, 4096, 64], causal,
+                     radius 256
 Inputs rotate over enough copies to exceed the 256 MB Infinity Cache (cold
 cache), the K timed steps are captured once in a HIP graph and replayed, and
 HIP events on the launch stream bracket the replay.  Rank 0 prints one JSON
@@ -38,7 +41,7 @@ METRIC = "attention fwd TFLOP/s (bf16) + % of MFMA peak, h=8 d_k=64 n=256 causal
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 CACHE_BYTES = 256 << 20       # Infinity Cache
-WORKLOAD_CFG = {"encoder": 2, "decoder": 3, "cross": 4, "block": 5, "decode": 6}
+WORKLOAD_CFG = {"encoder": 2, "decoder": 3, "cross": 4, "block": 5, "decode": 6, "window": 7}
 
 
 def legal_pairs(n_q, n_kv, causal, lq=None, lkv=None, batch=1):
@@ -294,6 +297,55 @@ def bench_block(K, W, args):
     return result, inp, flops
 
 
+def bench_window(K, W, args):
+    """Restricted self-attention at the block's shape: [4, 16, 4096, 64] bf16,
+    causal, radius 256 (each query sees at most 257 keys), cold inputs."""
+    import ctypes
+    import torch
+    import attn_inputs as gen
+    import head_attention_sdpa_amd as attn
+
+    L = attn.lib()
+    dev = torch.device("cuda:0")
+    B, H, n, r = 4, 16, 4096, 256
+    inp = gen.make_sdpa(f"window_causal_bf16_{B}x{H}x{n}x64_r{r}", "bf16", B, H, n, n, 64, 64, 0.125, True,
+                        cfg_id=7)
+    per_set = sum(a.nbytes for a in (inp.q_st, inp.k_st, inp.v_st)) + B * H * n * 64 * 2
+    R = max(1, math.ceil(2 * CACHE_BYTES / per_set)) if not args.hot else 1
+    base = [to_dev(a, "bf16", dev) for a in (inp.q_st, inp.k_st, inp.v_st)]
+    sets = [[t.clone() for t in base] for _ in range(R)]
+    outs = [torch.empty((B, H, n, 64), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+
+    def launch(s):
+        q, k, v = sets[s % R]
+        rc = L.attn_sdpa_window_fwd(attn.ATTN_BF16, B, H, n, n, 64, 64, q.data_ptr(), None, k.data_ptr(), None,
+                                    v.data_ptr(), None, outs[s % R].data_ptr(), None, 0.125,
+                                    attn.ATTN_MASK_CAUSAL, r, None, None, None,
+                                    torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"attn_sdpa_window_fwd failed: {attn.status_str(rc)}")
+
+    ms, _ = time_graph(launch, K, W, torch)
+    pairs = B * H * sum(min(i, r) + 1 for i in range(n))
+    flops = pairs * 256
+    algo_bytes = B * H * n * 64 * 2 * 4
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = algo_bytes / (ms * 1e-3) / 1e9
+    result = {
+        "value": tflops, "ms_per_step": ms, "pct_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "config": {"workload": inp.name, "batch": B, "heads": H, "n": n, "d_k": 64, "causal": True,
+                   "window_radius": r,
+                   "cache": f"{'hot' if args.hot else 'cold'}: {R} rotating input sets of {per_set / 1e6:.1f} MB",
+                   "timing": "HIP graph of the timed steps, HIP events on the launch stream",
+                   "flops_per_step": flops, "algorithmic_bytes_per_step": algo_bytes},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": read_traffic("window"),
+                     "kernel": "sdpa_fwd_bf16_d64 (band)", "algorithmic_bytes_per_launch": algo_bytes,
+                     "mfma_frac": tflops / PEAK_BF16_TFLOPS},
+    }
+    return result, inp, flops
+
+
 def bench_decode(K, W, args):
     """One decoding step over a key/value cache: 16 x 16 heads, one new query
     per sequence, cache capacity 4096 with lengths U{1024..4096}.  HBM-bound:
@@ -352,6 +404,14 @@ def cpu_baseline(cfg_id, inp, flops_full):
     """The oracle as it stands, on the host cores, on a bounded sample."""
     import oracle
     threads = oracle.default_threads()
+    if cfg_id == 7:
+        # sample: batch element 0, heads 0..3 (1/16 of the workload)
+        t0 = time.perf_counter()
+        oracle.sdpa(inp.q[:1, :4], inp.k[:1, :4], inp.v[:1, :4], scale=inp.scale, causal=True, window=256,
+                    nthreads=threads)
+        dt = time.perf_counter() - t0
+        return {"value": flops_full / 16 / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                "sample": "batch element 0, heads 0..3 (1/16), one run", "seconds": dt}
     if cfg_id == 6:
         best = float("inf")
         for _ in range(3):
@@ -426,6 +486,8 @@ def main():
         res, inp, flops = bench_block(K, W, args)
     elif cfg_id == 6:
         res, inp, flops = bench_decode(K, W, args)
+    elif cfg_id == 7:
+        res, inp, flops = bench_window(K, W, args)
     else:
         res, inp, flops = bench_sdpa(cfg_id, K, W, args)
     out = {"metric": METRIC, "value": res["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
