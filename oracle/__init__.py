@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
 and the ``cpu_baseline`` leg of ``bench.py``, never by the product package.
 It shares no code with the HIP path.  Functions: ``sdpa``, ``sdpa_rows``,
-``mha``, ``mha_rows``, ``linear``, ``decode`` and ``round_bf16``.
+``mha``, ``mha_rows``, ``linear``, ``decode``, ``sdpa_bwd`` and ``round_bf16``.
 
 The arithmetic lives in ``oracle.c`` (plain C, fp64, one query row at a time,
 sums in index order).  This module only marshals numpy arrays through ctypes.
@@ -56,13 +56,15 @@ def _load():
                                        _I, _I, i, i]
         lib.oracle_mha_rows_f64.argtypes = [i, i, i, i, i, i, i, _D, _D, _D, _D, _D, _D, _L,
                                             ctypes.c_int64, _D, d, i, _I, _I, i, i]
+        lib.oracle_sdpa_bwd_f64.argtypes = [i, i, i, i, i, i, _D, _D, _D, _D, _D, _D, _D, d, i, _I, _I, i]
         lib.oracle_sdpa_window_f64.argtypes = [i, i, i, i, i, i, _D, _D, _D, _D, _D, d, i, _I, _I, i, i]
         lib.oracle_decode_f64.argtypes = [i, i, i, i, i, i, _D, _D, _D, _D, _D, d, _I, i]
         lib.oracle_linear_f64.argtypes = [i, i, i, _D, ctypes.c_int64, _L, ctypes.c_int64, _D, _D, i]
         lib.oracle_round_bf16.argtypes = [d]
         lib.oracle_round_bf16.restype = d
         for f in ("oracle_sdpa_f64", "oracle_sdpa_rows_f64", "oracle_mha_f64", "oracle_mha_rows_f64",
-                  "oracle_linear_f64", "oracle_decode_f64", "oracle_sdpa_window_f64"):
+                  "oracle_linear_f64", "oracle_decode_f64", "oracle_sdpa_window_f64",
+                  "oracle_sdpa_bwd_f64"):
             getattr(lib, f).restype = i
         _lib = lib
     return _lib
@@ -202,6 +204,25 @@ def mha_rows(x_q, x_kv, w_q, w_k, w_v, w_o, heads, rows, scale=None, causal=Fals
                                      nthreads or default_threads())
     _check(rc, "oracle_mha_rows_f64")
     return y
+
+
+def sdpa_bwd(q, k, v, dout, scale=None, causal=False, seqlens_q=None, seqlens_kv=None, nthreads=None):
+    """Gradients of sum(dout * sdpa(q, k, v)) with respect to q, k and v, in
+    fp64, from the chain rule through the definition.  Returns (dq, dk, dv)."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, n_q, d_k = q.shape
+    n_kv, d_v = k.shape[2], v.shape[3]
+    if dout.shape != (B, H, n_q, d_v):
+        raise ValueError("dout must match the output shape")
+    scale = 1.0 / math.sqrt(d_k) if scale is None else float(scale)
+    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    lq, plq = _lens(seqlens_q, B)
+    lk, plk = _lens(seqlens_kv, B)
+    rc = _load().oracle_sdpa_bwd_f64(B, H, n_q, n_kv, d_k, d_v, _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), scale, int(bool(causal)), plq, plk,
+                                     nthreads or default_threads())
+    _check(rc, "oracle_sdpa_bwd_f64")
+    return dq, dk, dv
 
 
 def decode(q, k, v, scale=None, seqlens_kv=None, nthreads=None):

@@ -13,8 +13,9 @@
  *       vlmlib.cn summary and rockcohen.cc section 5.2), and
  *   (3) one projection of that block, y = x . W (no bias), and
  *   (4) one decoding step over a key/value cache (the newest n_q positions of
- *       each sequence under the causal mask), and
- *   (5) restricted self-attention over a neighbourhood of radius r.
+ *       each sequence under the causal mask),
+ *   (5) restricted self-attention over a neighbourhood of radius r, and
+ *   (6) the gradients of SDPA with respect to Q, K and V.
  *
  * Definitions followed literally, one query row at a time:
  *   legal(j)  <=>  j < n_kv  and  (no key lengths or j < L_kv[b])
@@ -253,6 +254,94 @@ int oracle_sdpa_rows_f64(int B, int H, int n_q, int n_kv, int d_k, int d_v, cons
     if (rows[r] < 0 || rows[r] >= (int64_t)B * H * n_q) return ORACLE_EINVAL;
   sdpa_ctx c = {B, H, n_q, n_kv, d_k, d_v, scale, causal, q, k, v, o, lse, seqlens_q, seqlens_kv, rows, 0, -1};
   return parallel_for(nrows, nthreads, n_kv > 0 ? n_kv : 1, sdpa_range, &c);
+}
+
+/* ---- SDPA backward -------------------------------------------------------- */
+/* Gradients of the loss sum_{i,c} dO[i,c] O[i,c] with respect to Q, K and V,
+ * written out from the chain rule through the definition above (the paper
+ * trains the model end to end: the vlmlib.cn summary's training-objective
+ * paragraph; attention-paper-guide section 05).  Per (b, h), for every valid
+ * query row i and its legal keys j, in index order:
+ *   P_ij = exp(s_ij - m_i) / Z_i                    (the forward weights)
+ *   O_i  = sum_j P_ij V_j,   D_i = sum_c dO_ic O_ic
+ *   dP_ij = sum_c dO_ic V_jc
+ *   dS_ij = P_ij (dP_ij - D_i)                      (softmax Jacobian)
+ *   dQ_i  = scale sum_j dS_ij K_j
+ *   dK_j += scale dS_ij Q_i,   dV_j += P_ij dO_i
+ * Padded query rows (i >= L_q) and illegal keys take no part: their O is a
+ * constant, so their gradients are zero. */
+typedef struct {
+  int B, H, n_q, n_kv, d_k, d_v; double scale; int causal;
+  const double *q, *k, *v, *dout; double *dq, *dk, *dv;
+  const int *seqlens_q, *seqlens_kv;
+} bwd_ctx;
+
+static void sdpa_bwd_range(void* p, int64_t begin, int64_t end, double* scratch) {
+  const bwd_ctx* c = (const bwd_ctx*)p;
+  double* P = scratch;                    /* n_kv */
+  double* O = scratch + c->n_kv;          /* d_v  */
+  for (int64_t bh = begin; bh < end; ++bh) {
+    int b = (int)(bh / c->H);
+    const double* Q = c->q + bh * c->n_q * c->d_k;
+    const double* K = c->k + bh * c->n_kv * c->d_k;
+    const double* V = c->v + bh * c->n_kv * c->d_v;
+    const double* dO = c->dout + bh * c->n_q * c->d_v;
+    double* dQ = c->dq + bh * c->n_q * c->d_k;
+    double* dK = c->dk + bh * c->n_kv * c->d_k;
+    double* dV = c->dv + bh * c->n_kv * c->d_v;
+    for (int64_t x = 0; x < (int64_t)c->n_q * c->d_k; ++x) dQ[x] = 0.0;
+    for (int64_t x = 0; x < (int64_t)c->n_kv * c->d_k; ++x) dK[x] = 0.0;
+    for (int64_t x = 0; x < (int64_t)c->n_kv * c->d_v; ++x) dV[x] = 0.0;
+    int Lq = c->seqlens_q ? c->seqlens_q[b] : c->n_q;
+    int Lkv = c->seqlens_kv ? c->seqlens_kv[b] : c->n_kv;
+    for (int i = 0; i < Lq; ++i) {
+      int jend = Lkv;
+      if (c->causal && i + 1 < jend) jend = i + 1;
+      if (jend <= 0) continue;                          /* no legal key: O = 0, no gradient */
+      const double* qi = Q + (int64_t)i * c->d_k;
+      const double* doi = dO + (int64_t)i * c->d_v;
+      double m = -INFINITY;
+      for (int j = 0; j < jend; ++j) {                  /* scores and their max */
+        double dot = 0.0;
+        for (int x = 0; x < c->d_k; ++x) dot += qi[x] * K[(int64_t)j * c->d_k + x];
+        P[j] = c->scale * dot;
+        if (P[j] > m) m = P[j];
+      }
+      double Z = 0.0;
+      for (int j = 0; j < jend; ++j) { P[j] = exp(P[j] - m); Z += P[j]; }
+      for (int j = 0; j < jend; ++j) P[j] /= Z;
+      for (int x = 0; x < c->d_v; ++x) O[x] = 0.0;
+      for (int j = 0; j < jend; ++j)
+        for (int x = 0; x < c->d_v; ++x) O[x] += P[j] * V[(int64_t)j * c->d_v + x];
+      double D = 0.0;
+      for (int x = 0; x < c->d_v; ++x) D += doi[x] * O[x];
+      double* dqi = dQ + (int64_t)i * c->d_k;
+      for (int j = 0; j < jend; ++j) {
+        const double* vj = V + (int64_t)j * c->d_v;
+        double dp = 0.0;
+        for (int x = 0; x < c->d_v; ++x) dp += doi[x] * vj[x];
+        double ds = P[j] * (dp - D);
+        const double* kj = K + (int64_t)j * c->d_k;
+        double* dkj = dK + (int64_t)j * c->d_k;
+        double* dvj = dV + (int64_t)j * c->d_v;
+        for (int x = 0; x < c->d_k; ++x) dqi[x] += c->scale * ds * kj[x];
+        for (int x = 0; x < c->d_k; ++x) dkj[x] += c->scale * ds * qi[x];
+        for (int x = 0; x < c->d_v; ++x) dvj[x] += P[j] * doi[x];
+      }
+    }
+  }
+}
+
+/* q, k, v, dout as in oracle_sdpa_f64 (dout [B,H,n_q,d_v]); writes dq, dk, dv
+ * of the same shapes as q, k, v. */
+int oracle_sdpa_bwd_f64(int B, int H, int n_q, int n_kv, int d_k, int d_v, const double* q,
+                        const double* k, const double* v, const double* dout, double* dq, double* dk,
+                        double* dv, double scale, int causal, const int* seqlens_q,
+                        const int* seqlens_kv, int nthreads) {
+  if (B < 0 || H < 0 || n_q < 0 || n_kv < 0 || d_k < 1 || d_v < 1 || !(scale > 0.0)) return ORACLE_EINVAL;
+  if (!check_lengths(seqlens_q, B, n_q) || !check_lengths(seqlens_kv, B, n_kv)) return ORACLE_EINVAL;
+  bwd_ctx c = {B, H, n_q, n_kv, d_k, d_v, scale, causal, q, k, v, dout, dq, dk, dv, seqlens_q, seqlens_kv};
+  return parallel_for((int64_t)B * H, nthreads, (int64_t)n_kv + d_v + 1, sdpa_bwd_range, &c);
 }
 
 /* ---- dense product C[r,:] = A[r,:] . W  (W row-major [K][N]) ------------- */

@@ -36,6 +36,11 @@ MUTATIONS = {
     "window one short on the left": ("legal_begin = i - c->window;", "legal_begin = i - c->window + 1;"),
     "window one long on the right": ("if (i + c->window + 1 < legal_end) legal_end = i + c->window + 1;",
                                      "if (i + c->window + 2 < legal_end) legal_end = i + c->window + 2;"),
+    "bwd softmax Jacobian without D": ("double ds = P[j] * (dp - D);", "double ds = P[j] * dp;"),
+    "bwd dK without scale": ("for (int x = 0; x < c->d_k; ++x) dkj[x] += c->scale * ds * qi[x];",
+                             "for (int x = 0; x < c->d_k; ++x) dkj[x] += ds * qi[x];"),
+    "bwd dV from the wrong weight": ("for (int x = 0; x < c->d_v; ++x) dvj[x] += P[j] * doi[x];",
+                                     "for (int x = 0; x < c->d_v; ++x) dvj[x] += ds * doi[x];"),
     "projection weight transposed": ("for (int n = 0; n < g->N; ++n) c[n] += ak * wk[n];",
                                      "for (int n = 0; n < g->N; ++n) c[n] += ak * g->w[(int64_t)n * g->K + kk];"),
 }

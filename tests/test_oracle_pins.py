@@ -460,3 +460,70 @@ def test_window_equals_attention_over_the_neighbourhood():
                 ref, rl = oracle.sdpa(q[b:b + 1, :, i:i + 1], k[b:b + 1, :, lo:hi], v[b:b + 1, :, lo:hi])
                 assert np.abs(o[b, :, i] - ref[0, :, 0]).max() < 1e-13
                 assert np.abs(lse[b, :, i] - rl[0, :, 0]).max() < 1e-13
+
+
+# ---------------------------------------------------------------------------
+# Gradients of SDPA (the model is trained end to end: the vlmlib.cn summary's
+# training-objective paragraph, attention-paper-guide section 05)
+# ---------------------------------------------------------------------------
+def _fd_grads(q, k, v, dout, h=1e-5, **kw):
+    """Central finite differences of L = sum(dout * O) through the forward
+    oracle (pinned above), element by element."""
+    def loss(q_, k_, v_):
+        return float((dout * oracle.sdpa(q_, k_, v_, **kw)[0]).sum())
+    grads = []
+    for which in range(3):
+        base = [q, k, v]
+        g = np.zeros_like(base[which])
+        it = np.nditer(base[which], flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            plus = [a.copy() for a in base]
+            minus = [a.copy() for a in base]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            g[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+        grads.append(g)
+    return grads
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_matches_finite_differences(causal):
+    """The analytic gradients agree with central differences of the forward
+    (error O(h^2) ~ 1e-9).  Catches a dropped softmax-Jacobian term, a wrong
+    sign, a missing scale, a transposed product or a wrong mask in the
+    backward."""
+    B, H, n_q, n_kv, d = 1, 2, 5, 6, 3
+    q, k, v = rnd(600, (B, H, n_q, d)), rnd(601, (B, H, n_kv, d)), rnd(602, (B, H, n_kv, d))
+    dout = rnd(603, (B, H, n_q, d))
+    kw = dict(scale=0.7, causal=causal)
+    dq, dk, dv = oracle.sdpa_bwd(q, k, v, dout, **kw)
+    fq, fk, fv = _fd_grads(q, k, v, dout, **kw)
+    for a, b_ in ((dq, fq), (dk, fk), (dv, fv)):
+        assert np.abs(a - b_).max() < 1e-7 * (1 + np.abs(b_).max())
+
+
+def test_bwd_with_lengths_matches_finite_differences():
+    B, H, n_q, n_kv, d = 2, 1, 5, 6, 3
+    q, k, v = rnd(610, (B, H, n_q, d)), rnd(611, (B, H, n_kv, d)), rnd(612, (B, H, n_kv, d))
+    dout = rnd(613, (B, H, n_q, d))
+    kw = dict(scale=0.5, causal=True, seqlens_q=np.array([5, 3], np.int32),
+              seqlens_kv=np.array([6, 2], np.int32))
+    dq, dk, dv = oracle.sdpa_bwd(q, k, v, dout, **kw)
+    fq, fk, fv = _fd_grads(q, k, v, dout, **kw)
+    for a, b_ in ((dq, fq), (dk, fk), (dv, fv)):
+        assert np.abs(a - b_).max() < 1e-7 * (1 + np.abs(b_).max())
+    # padded query rows and keys past the length get exactly zero gradient
+    assert np.all(dq[1, :, 3:] == 0) and np.all(dk[1, :, 2:] == 0) and np.all(dv[1, :, 2:] == 0)
+
+
+def test_bwd_special_cases():
+    """One key: the weight is the constant 1, so dQ = dK = 0 and dV = sum_i dO_i.
+    Zero dO gives zero gradients."""
+    q, k, v = rnd(620, (1, 2, 4, 5)), rnd(621, (1, 2, 1, 5)), rnd(622, (1, 2, 1, 5))
+    dout = rnd(623, (1, 2, 4, 5))
+    dq, dk, dv = oracle.sdpa_bwd(q, k, v, dout)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    assert np.allclose(dv[0, :, 0], dout[0].sum(axis=1), rtol=0, atol=1e-13)
+    z = oracle.sdpa_bwd(q, k, v, np.zeros_like(dout))
+    assert all(np.all(g == 0) for g in z)
