@@ -266,3 +266,27 @@ def decode_workload(**overrides):
          else np.asarray(p["L"], dtype=np.int32))
     return make_sdpa(f"decode_bf16_{p['B']}x{p['H']}x{p['n_q']}q_cache{p['n_kv']}", "bf16", p["B"],
                      p["H"], p["n_q"], p["n_kv"], 64, 64, 0.125, False, seqlens_kv=L, cfg_id=6)
+
+
+def make_dout(inp: SDPAInputs, cfg_id: int) -> tuple[np.ndarray, np.ndarray]:
+    """Gradient at the attention output for a backward pass over `inp`: iid
+    N(0,1) rounded to the inputs' dtype, seed 1000*cfg_id + 8, rows beyond the
+    query lengths NaN.  Returns (exact fp64 values, storage array)."""
+    B, H, n_q, _, _, d_v = inp.shape
+    g = to_dtype(normal(_seed(cfg_id, 8), (B, H, n_q, d_v)), inp.dtype)
+    if inp.seqlens_q is not None:
+        for b in range(B):
+            g[b, :, inp.seqlens_q[b]:, :] = np.nan
+    return g, storage(g, inp.dtype)
+
+
+def backward_workload(**overrides) -> tuple[SDPAInputs, np.ndarray, np.ndarray]:
+    """Gradients of the block's attention: [4,16,4096,64] bf16, causal, scale
+    1/8, Q/K/V and dO iid N(0,1) (the per-head shape of the multi-head block,
+    workload 5).  Seeds 1000*8 + t.  `overrides` may shrink any size."""
+    p = dict(B=4, H=16, n=4096)
+    p.update(overrides)
+    inp = make_sdpa(f"backward_bf16_{p['B']}x{p['H']}x{p['n']}x64_causal", "bf16", p["B"], p["H"],
+                    p["n"], p["n"], 64, 64, 0.125, True, cfg_id=8)
+    g, g_st = make_dout(inp, 8)
+    return inp, g, g_st

@@ -2,7 +2,7 @@
 """Benchmark of the attention forward hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload decoder|encoder|cross|block|decode|window]
+                    [--workload decoder|encoder|cross|block|decode|window|backward]
 
 A step is one pass of the hot path over one batch of synthetic input that is
 already resident in HBM:
@@ -15,6 +15,8 @@ already resident in HBM:
                      one new query each, cache 4096 with lengths U{1024..4096}
   window             restricted self-attention, [4, 16, 4096, 64], causal,
                      radius 256
+  backward           gradients dQ, dK, dV of causal attention at the block's
+                     shape, [4, 16, 4096, 64] (the forward's o and lse given)
 Inputs rotate over enough copies to exceed the 256 MB Infinity Cache (cold
 cache), the K timed steps are captured once in a HIP graph and replayed, and
 HIP events on the launch stream bracket the replay.  Rank 0 prints one JSON
@@ -41,7 +43,7 @@ METRIC = "attention fwd TFLOP/s (bf16) + % of MFMA peak, h=8 d_k=64 n=256 causal
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 CACHE_BYTES = 256 << 20       # Infinity Cache
-WORKLOAD_CFG = {"encoder": 2, "decoder": 3, "cross": 4, "block": 5, "decode": 6, "window": 7}
+WORKLOAD_CFG = {"encoder": 2, "decoder": 3, "cross": 4, "block": 5, "decode": 6, "window": 7, "backward": 8}
 
 
 def legal_pairs(n_q, n_kv, causal, lq=None, lkv=None, batch=1):
@@ -400,10 +402,79 @@ def bench_decode(K, W, args):
     return result, inp, flops
 
 
+def bench_backward(K, W, args):
+    """Gradients of causal attention at the block's shape, [4, 16, 4096, 64]
+    bf16: one attn_sdpa_bwd call per step (D and lse preprocessing, the dK/dV
+    kernel, the dQ kernel), given q, k, v, the forward's o and lse, and dO.
+    Work is counted algorithmically, 10*d FLOPs per legal pair (the products
+    Q.K^T, dO.V^T, P^T.dO, dS^T.Q and dS.K); the kernels recompute Q.K^T and
+    dO.V^T once more in the dQ pass (14*d executed)."""
+    import torch
+    import attn_inputs as gen
+    import head_attention_sdpa_amd as attn
+
+    L = attn.lib()
+    dev = torch.device("cuda:0")
+    inp, g, g_st = gen.backward_workload()
+    B, H, n, _, d, _ = inp.shape
+    tensor_bytes = B * H * n * d * 2
+    per_set = 8 * tensor_bytes + B * H * n * 4
+    R = max(1, math.ceil(2 * CACHE_BYTES / per_set)) if not args.hot else 1
+    base = [to_dev(a, "bf16", dev) for a in (inp.q_st, inp.k_st, inp.v_st, g_st)]
+    sets = []
+    for _ in range(R):
+        q, k, v, do = (t.clone() for t in base)
+        o, lse = attn.sdpa(q, k, v, scale=inp.scale, causal=True, return_lse=True)
+        grads = [torch.empty_like(t) for t in (q, k, v)]
+        sets.append((q, k, v, o, lse, do, grads))
+    nbytes = attn.sdpa_bwd_workspace_bytes(B, H, n, n)
+    work = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+    def launch(s):
+        q, k, v, o, lse, do, (dq, dk, dv) = sets[s % R]
+        rc = L.attn_sdpa_bwd(attn.ATTN_BF16, B, H, n, n, d, d, q.data_ptr(), None, k.data_ptr(), None,
+                             v.data_ptr(), None, o.data_ptr(), None, do.data_ptr(), None, lse.data_ptr(),
+                             dq.data_ptr(), None, dk.data_ptr(), None, dv.data_ptr(), None, float(inp.scale),
+                             attn.ATTN_MASK_CAUSAL, None, None, work.data_ptr(), nbytes,
+                             torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"attn_sdpa_bwd failed: {attn.status_str(rc)}")
+
+    ms, _ = time_graph(launch, K, W, torch)
+    pairs = B * H * n * (n + 1) // 2
+    flops = pairs * 10 * d
+    tflops = flops / (ms * 1e-3) / 1e12
+    algo_bytes = 8 * tensor_bytes + B * H * n * 4
+    result = {
+        "metric": "attention bwd TFLOP/s (bf16) + % of MFMA peak, h=16 d_k=64 n=4096 causal",
+        "value": tflops, "ms_per_step": ms, "pct_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "config": {"workload": inp.name, "batch": B, "heads": H, "n": n, "d_k": d, "causal": True,
+                   "cache": f"{'hot' if args.hot else 'cold'}: {R} rotating input sets of {per_set / 1e6:.1f} MB",
+                   "timing": "HIP graph of the timed steps, HIP events on the launch stream",
+                   "flops_per_step": flops, "flops_counted": "10*d per legal pair",
+                   "algorithmic_bytes_per_step": algo_bytes},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / PEAK_BF16_TFLOPS, "traffic": read_traffic("backward"),
+                     "kernel": "attn_sdpa_bwd (sdpa_bwd_pre + sdpa_bwd_dkdv + sdpa_bwd_dq), timed as one call",
+                     "algorithmic_flops_per_launch": flops,
+                     "hbm_frac": algo_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+    }
+    inp.dout = g
+    return result, inp, flops
+
+
 def cpu_baseline(cfg_id, inp, flops_full):
     """The oracle as it stands, on the host cores, on a bounded sample."""
     import oracle
     threads = oracle.default_threads()
+    if cfg_id == 8:
+        # sample: batch element 0, heads 0..7 (1/8 of the workload)
+        t0 = time.perf_counter()
+        oracle.sdpa_bwd(inp.q[:1, :8], inp.k[:1, :8], inp.v[:1, :8], inp.dout[:1, :8], scale=inp.scale,
+                        causal=True, nthreads=threads)
+        dt = time.perf_counter() - t0
+        return {"value": flops_full / 8 / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                "sample": "batch element 0, heads 0..7 (1/8), one run", "seconds": dt}
     if cfg_id == 7:
         # sample: batch element 0, heads 0..3 (1/16 of the workload)
         t0 = time.perf_counter()
@@ -488,9 +559,11 @@ def main():
         res, inp, flops = bench_decode(K, W, args)
     elif cfg_id == 7:
         res, inp, flops = bench_window(K, W, args)
+    elif cfg_id == 8:
+        res, inp, flops = bench_backward(K, W, args)
     else:
         res, inp, flops = bench_sdpa(cfg_id, K, W, args)
-    out = {"metric": METRIC, "value": res["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+    out = {"metric": res.get("metric", METRIC), "value": res["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
            "warmup": W, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": res["config"], "pct_mfma_peak": res["pct_mfma_peak"],

@@ -29,7 +29,8 @@ STATUS = {0: "ATTN_OK", -1: "ATTN_E_INVALID", -2: "ATTN_E_UNSUPPORTED", -3: "ATT
 
 # every entry point that include/attn_sdpa.h declares
 EXPORTS = ("attn_sdpa_fwd", "attn_sdpa_window_fwd", "attn_mha_workspace_bytes", "attn_mha_fwd", "attn_decode_workspace_bytes",
-           "attn_decode_fwd", "attn_linear_fwd", "attn_status_str", "attn_abi_version")
+           "attn_decode_fwd", "attn_linear_fwd", "attn_sdpa_bwd_workspace_bytes", "attn_sdpa_bwd",
+           "attn_status_str", "attn_abi_version")
 
 
 class AttnError(RuntimeError):
@@ -72,6 +73,12 @@ def lib() -> ctypes.CDLL:
         L.attn_decode_fwd.restype = i
         L.attn_linear_fwd.argtypes = [i, i, i, i, vp, ctypes.c_int64, vp, vp, ctypes.c_int64, vp]
         L.attn_linear_fwd.restype = i
+        L.attn_sdpa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+        L.attn_sdpa_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_sdpa_bwd.argtypes = [i, i, i, i, i, i, i, vp, sp, vp, sp, vp, sp, vp, sp, vp, sp, vp,
+                                    vp, sp, vp, sp, vp, sp, ctypes.c_float, i, vp, vp, vp,
+                                    ctypes.c_size_t, vp]
+        L.attn_sdpa_bwd.restype = i
         L.attn_status_str.argtypes = [i]
         L.attn_status_str.restype = ctypes.c_char_p
         L.attn_abi_version.argtypes = []
@@ -252,3 +259,50 @@ def linear(x, w, out=None, stream=None):
                                max(out.stride(0), n), _stream(stream))
     _check("attn_linear_fwd", rc)
     return out
+
+
+def sdpa_bwd_workspace_bytes(batch, heads, n_q, n_kv, d_k=64, d_v=64, dtype=ATTN_BF16) -> int:
+    return int(lib().attn_sdpa_bwd_workspace_bytes(dtype, batch, heads, n_q, n_kv, d_k, d_v))
+
+
+def sdpa_bwd(q, k, v, o, lse, dout, scale=None, causal=False, seqlens_q=None, seqlens_kv=None,
+             dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients of scaled dot-product attention (bf16, head size 64): given
+    the forward's q, k, v, its output o and lse [B,H,n_q] (fp32, contiguous)
+    and the gradient dout of o, returns (dq, dk, dv).  scale, causal and the
+    lengths must be those of the forward call."""
+    torch = _torch()
+    B, H, n_q, d_k = q.shape
+    n_kv, d_v = k.shape[2], v.shape[3]
+    if k.shape != (B, H, n_kv, d_k) or v.shape != (B, H, n_kv, d_v):
+        raise ValueError("shape mismatch between q, k, v")
+    if o.shape != (B, H, n_q, d_v) or dout.shape != o.shape:
+        raise ValueError("o and dout must be [B, H, n_q, d_v]")
+    if not (lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == (B, H, n_q)):
+        raise ValueError("lse must be a contiguous fp32 [B, H, n_q] tensor")
+    for t in (k, v, o, dout, lse):
+        if t.device != q.device:
+            raise ValueError("all tensors must be on the same device")
+    if q.device.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    dt = _dtype_code(q)
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    nbytes = sdpa_bwd_workspace_bytes(B, H, n_q, n_kv, d_k, d_v, dt)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    st = [_strides4(t) for t in (q, k, v, o, dout, dq, dk, dv)]
+    ptr = [t.data_ptr() or None for t in (q, k, v, o, dout, dq, dk, dv)]
+    rc = lib().attn_sdpa_bwd(dt, B, H, n_q, n_kv, d_k, d_v,
+                             ptr[0], ctypes.byref(st[0]), ptr[1], ctypes.byref(st[1]),
+                             ptr[2], ctypes.byref(st[2]), ptr[3], ctypes.byref(st[3]),
+                             ptr[4], ctypes.byref(st[4]), lse.data_ptr() or None,
+                             ptr[5], ctypes.byref(st[5]), ptr[6], ctypes.byref(st[6]),
+                             ptr[7], ctypes.byref(st[7]), 0.0 if scale is None else float(scale),
+                             ATTN_MASK_CAUSAL if causal else ATTN_MASK_NONE,
+                             _lens_ptr(seqlens_q, B, q.device), _lens_ptr(seqlens_kv, B, q.device),
+                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                             _stream(stream))
+    _check("attn_sdpa_bwd", rc)
+    return dq, dk, dv

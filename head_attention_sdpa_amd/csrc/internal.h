@@ -52,6 +52,33 @@ struct SdpaDecodeParams {
 // Chunking of the decoding step for these sizes (the workspace depends on it).
 void sdpa_decode_plan(int batch, int heads, int n_kv, int* chunk_tiles, int* n_chunks);
 
+// Gradients of scaled dot-product attention, bf16 storage, head size 64.
+struct SdpaBwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;            // forward output
+  const uint16_t* dout;         // gradient of the loss with respect to o
+  const float* lse;             // forward log-sum-exp [batch*heads*n_q] (natural log)
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* ld;                    // workspace [batch*heads*n_q][2]: lse*log2(e) (+inf: no weight), D = dO.O
+  const int32_t* seqlens_q;
+  const int32_t* seqlens_kv;
+  int64_t qs_b, qs_h, qs_n;
+  int64_t ks_b, ks_h, ks_n;
+  int64_t vs_b, vs_h, vs_n;
+  int64_t os_b, os_h, os_n;
+  int64_t dos_b, dos_h, dos_n;
+  int64_t dqs_b, dqs_h, dqs_n;
+  int64_t dks_b, dks_h, dks_n;
+  int64_t dvs_b, dvs_h, dvs_n;
+  int batch, heads, n_q, n_kv;
+  float scale, scale_log2;
+  int causal;
+};
+
 // Scaled dot-product attention, fp32 storage and arithmetic, head sizes <= 64.
 struct SdpaF32Params {
   const float* q;
@@ -88,6 +115,7 @@ struct GemmBf16Params {
 hipError_t launch_sdpa_bf16(const SdpaBf16Params& p, hipStream_t stream);
 hipError_t launch_sdpa_f32(const SdpaF32Params& p, hipStream_t stream);
 hipError_t launch_sdpa_decode_bf16(const SdpaDecodeParams& p, hipStream_t stream);
+hipError_t launch_sdpa_bwd_bf16(const SdpaBwdParams& p, hipStream_t stream);
 hipError_t launch_gemm_bf16(const GemmBf16Params& p, hipStream_t stream);
 bool gemm_bf16_main_supported(const GemmBf16Params& p);   // shapes the fast kernel takes
 

@@ -1,0 +1,456 @@
+// Gradients of scaled dot-product attention, bf16 storage, head size 64, gfx950.
+//
+// The model of "Attention Is All You Need" is trained end to end (the vlmlib.cn
+// summary's training-objective paragraph; attention-paper-guide section 05), so
+// the attention layer needs dQ, dK and dV for a given dO.  With P the forward
+// weights and D_i = sum_c dO_ic O_ic (the softmax Jacobian applied to dO):
+//   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),   dQ = scale dS K,
+//   dK = scale dS^T Q.
+// P is recomputed from the scores and the forward's log-sum-exp, exp(s - lse),
+// so nothing of size n_q x n_kv is stored.  Three kernels:
+//
+//   sdpa_bwd_pre       per query row: D (fp32) and lse in log2 units (+inf for
+//                      padded rows and rows without keys, so their weights are
+//                      exactly 0), into the workspace.
+//   sdpa_bwd_dkdv      workgroup = (b, h, 128 keys), wave w owns 32 keys and
+//                      keeps their K and V fragments in registers; query tiles
+//                      of 64 (Q, dO and the per-row terms) stream through an
+//                      LDS-DMA ring.  Per tile and 32-query block the wave
+//                      computes S = Q K^T and dP = dO V^T with one key per lane
+//                      column, then dV^T += dO^T P and dK^T += Q^T dS with the
+//                      score accumulators as the B operands (their rows are
+//                      the queries in the order the C layout gives them; the
+//                      dO^T and Q^T operands are read transposed in the same
+//                      order).
+//   sdpa_bwd_dq        workgroup = (b, h, 128 queries), the forward's
+//                      decomposition: S^T = K Q^T and dP^T = V dO^T with one
+//                      query per lane column, dQ^T += K^T dS^T.
+//
+// Every product is v_mfma_f32_32x32x16_bf16 (fp32 accumulation); P and dS are
+// rounded to bf16 for the products, and dQ, dK, dV once to bf16 at the store.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace attn {
+namespace {
+
+constexpr int D = 64;          // head size (d_k = d_v)
+constexpr int BT = 64;         // rows per streamed tile (queries or keys)
+constexpr int TILE_E = BT * D; // bf16 elements of one [64][64] tile (8 KiB)
+constexpr float LOG2E = 1.4426950408889634f;
+
+// A [32 x 16] operand (rows r0 + lane%32, columns 16*dstep + 8*g + 0..7) read
+// from a row-major [64][64] tile stored with the swz_k chunk swizzle.
+__device__ __forceinline__ bf16x8 rows_frag(const __bf16* tile, int r, int dstep, int g) {
+  const int c = 2 * dstep + g;
+  return *reinterpret_cast<const bf16x8*>(tile + r * D + 8 * (c ^ swz_k(r)));
+}
+
+// The transposed operand of block (cb, jb, s): element t of lane l is
+// tile[row(t)][32*cb + l%32] with row(t) = 32*jb + 16*s + 8*(t/4) + 4*g + t%4,
+// the row order of the score accumulator's C layout, read with two
+// ds_read_b64_tr_b16 from the swz_k-swizzled tile.
+__device__ __forceinline__ bf16x8 tr_frag(const __bf16* tile, int cb, int jb, int s, int lane) {
+  const int k16 = lane & 15, g = lane >> 5;
+  const int chalf = (lane >> 4) & 1;
+  const int tr_row = g * 4 + (k16 >> 2);
+  const int tr_chunk = 2 * chalf + ((k16 & 3) >> 1);
+  const int tr_half = 4 * (k16 & 1);
+  bf16x4 part[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int row = 32 * jb + 16 * s + 8 * hh + tr_row;
+    part[hh] = tr_read(tile + row * D + tr_half + 8 * ((4 * cb + tr_chunk) ^ swz_k(row)));
+  }
+  return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Registers 8s..8s+7 of an accumulator, rounded to bf16, as an MFMA operand.
+__device__ __forceinline__ bf16x8 pack8(const float* x) {
+  bf16x8 r;
+#pragma unroll
+  for (int t = 0; t < 8; t += 2) {
+    const bf16x2 h = __builtin_convertvector(f32x2{x[t], x[t + 1]}, bf16x2);
+    r[t] = h[0];
+    r[t + 1] = h[1];
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// 8 lanes per query row: D = dO . O (fp32) and the log2-unit lse.
+__global__ __launch_bounds__(256) void sdpa_bwd_pre(const SdpaBwdParams p) {
+  const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int sub = threadIdx.x & 7;
+  const int64_t rows = (int64_t)p.batch * p.heads * p.n_q;
+  if (row >= rows) return;                      // whole 8-lane groups leave together
+  const int i = (int)(row % p.n_q);
+  const int64_t bh = row / p.n_q;
+  const int b = (int)(bh / p.heads), h = (int)(bh - (int64_t)b * p.heads);
+  int Lq = p.n_q;
+  if (p.seqlens_q) Lq = min(max(p.seqlens_q[b], 0), p.n_q);
+  const __bf16* orow = reinterpret_cast<const __bf16*>(p.o) + b * p.os_b + h * p.os_h + (int64_t)i * p.os_n;
+  const __bf16* drow = reinterpret_cast<const __bf16*>(p.dout) + b * p.dos_b + h * p.dos_h + (int64_t)i * p.dos_n;
+  const bf16x8 ov = *reinterpret_cast<const bf16x8*>(orow + 8 * sub);
+  const bf16x8 dv = *reinterpret_cast<const bf16x8*>(drow + 8 * sub);
+  float dot = 0.f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) dot = fmaf((float)ov[t], (float)dv[t], dot);
+  dot += __shfl_xor(dot, 1, 8);
+  dot += __shfl_xor(dot, 2, 8);
+  dot += __shfl_xor(dot, 4, 8);
+  if (sub == 0) {
+    const float lse = p.lse[row];
+    const bool valid = i < Lq && lse > -INFINITY;
+    *reinterpret_cast<f32x2*>(p.ld + 2 * row) = valid ? f32x2{lse * LOG2E, dot} : f32x2{INFINITY, 0.f};
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int NS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void sdpa_bwd_dkdv(const SdpaBwdParams p) {
+  constexpr int BK = 128;                  // keys per workgroup (4 waves x 32)
+  constexpr int STAGE_E = 2 * TILE_E;      // Q tile, dO tile
+  constexpr int IPT = 5;                   // DMA instructions per wave per stage: 4 of Q/dO, 1 of (lse2, D)
+  static_assert(NS >= 2 && NS <= 4, "bad configuration");
+  __shared__ __attribute__((aligned(1024))) __bf16 smem[NS * STAGE_E];
+  __shared__ __attribute__((aligned(1024))) float lds_ld[NS][4][256];   // per stage, per wave: 128 (lse2, D)
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i32 = lane & 31, g = lane >> 5;
+  const int bhn = p.batch * p.heads;
+  const int kb = blockIdx.x / bhn;          // key blocks in ascending order: the longest causal ones first
+  const int bh = blockIdx.x - kb * bhn;
+  const int b = bh / p.heads, h = bh - b * p.heads;
+  int Lq = p.n_q, Lkv = p.n_kv;
+  if (p.seqlens_q) Lq = min(max(p.seqlens_q[b], 0), p.n_q);
+  if (p.seqlens_kv) Lkv = min(max(p.seqlens_kv[b], 0), p.n_kv);
+
+  const int k0 = kb * BK, kw0 = k0 + 32 * wave;
+  const int kj = kw0 + i32;                 // this lane's key
+  // query tiles the workgroup visits: causal ones start at the block's first key
+  int qt_begin = p.causal ? k0 / BT : 0;
+  int nqt = k0 < Lkv ? (Lq + BT - 1) / BT - qt_begin : 0;
+  if (nqt < 0) nqt = 0;
+
+  const __bf16* Qb = reinterpret_cast<const __bf16*>(p.q) + b * p.qs_b + h * p.qs_h;
+  const __bf16* Ob = reinterpret_cast<const __bf16*>(p.dout) + b * p.dos_b + h * p.dos_h;
+  const float* LDb = p.ld + (int64_t)bh * p.n_q * 2;
+  const uint32_t q_bytes = Lq > 0 ? (uint32_t)((int64_t)(Lq - 1) * p.qs_n * 2 + 128) : 0u;
+  const uint32_t o_bytes = Lq > 0 ? (uint32_t)((int64_t)(Lq - 1) * p.dos_n * 2 + 128) : 0u;
+  const uint32_t ld_bytes = (uint32_t)p.n_q * 8;
+
+  // K and V fragments of the wave's 32 keys (B operands: lane = key, k = d);
+  // keys past the length read as zeros.
+  bf16x8 kf[4], vf[4];
+  {
+    const bool kvalid = kj < Lkv;
+    const int jj = kvalid ? kj : 0;
+    const __bf16* krow = reinterpret_cast<const __bf16*>(p.k) + b * p.ks_b + h * p.ks_h + (int64_t)jj * p.ks_n;
+    const __bf16* vrow = reinterpret_cast<const __bf16*>(p.v) + b * p.vs_b + h * p.vs_h + (int64_t)jj * p.vs_n;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const bf16x8 kk = *reinterpret_cast<const bf16x8*>(krow + 16 * d + 8 * g);
+      const bf16x8 vv = *reinterpret_cast<const bf16x8*>(vrow + 16 * d + 8 * g);
+      kf[d] = kvalid ? kk : bf16x8{};
+      vf[d] = kvalid ? vv : bf16x8{};
+    }
+    // consume them here: the wait for these loads happens once, before any DMA
+#pragma unroll
+    for (int d = 0; d < 4; ++d) asm volatile("" ::"v"(kf[d]), "v"(vf[d]));
+  }
+
+  // DMA offsets: instruction u (0..15) of a stage covers row block u & 7 of Q
+  // (u < 8) or dO; the fifth instruction of each wave copies 128 (lse2, D)
+  // pairs into the wave's own slot.
+  uint32_t dma_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int u = wave * 4 + i;
+    const bool is_o = u >= 8;
+    const int r = 8 * (u & 7) + (lane >> 3);
+    const int c = (lane & 7) ^ swz_k(r);
+    dma_off[i] = (uint32_t)(((int64_t)r * (is_o ? p.dos_n : p.qs_n) + c * 8) * 2);
+  }
+  auto issue_stage = [&](int j) {
+    const int q0 = (qt_begin + j) * BT;
+    const int64_t q_adv = (int64_t)q0 * p.qs_n, o_adv = (int64_t)q0 * p.dos_n;
+    const i32x4 rq = make_rsrc(Qb + q_adv, (uint32_t)max<int64_t>(0, (int64_t)q_bytes - 2 * q_adv));
+    const i32x4 ro = make_rsrc(Ob + o_adv, (uint32_t)max<int64_t>(0, (int64_t)o_bytes - 2 * o_adv));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = wave * 4 + i;
+      const bool is_o = u >= 8;
+      const __bf16* dst = smem + (j % NS) * STAGE_E + (is_o ? TILE_E : 0) + (u & 7) * 512;
+      dma16(dma_off[i], is_o ? ro : rq, lds_addr(dst));
+    }
+    const i32x4 rl = make_rsrc(LDb + 2 * (int64_t)q0, (uint32_t)max<int64_t>(0, (int64_t)ld_bytes - 8 * (int64_t)q0));
+    dma16((uint32_t)(lane * 16), rl, lds_addr(&lds_ld[j % NS][wave][0]));
+  };
+
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < nqt) issue_stage(j);
+
+  f32x16 dk0 = {}, dk1 = {}, dv0 = {}, dv1 = {};   // dK^T, dV^T: d 0..31 / 32..63, lane = key
+  const float c2 = p.scale_log2;
+
+  for (int t = 0; t < nqt; ++t) {
+    wait_vmcnt_le<IPT>(min(NS - 2, nqt - 1 - t) * IPT);
+    barrier_lds();   // stage t visible; every wave is done with stage t-1
+    if (t + NS - 1 < nqt) issue_stage(t + NS - 1);
+    const int q0 = (qt_begin + t) * BT;
+    if (p.causal && q0 + BT - 1 < kw0) continue;   // wave-uniform: every query before the wave's keys
+    const __bf16* Qs = smem + (t % NS) * STAGE_E;
+    const __bf16* Ds = Qs + TILE_E;
+    const float* lt = &lds_ld[t % NS][wave][0];
+    const bool need_mask = (p.causal && q0 < kw0 + 32) || q0 + BT > Lq || kw0 + 32 > Lkv;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      // S = Q K^T and dP = dO V^T for queries q0 + 32*qb + row(r): lane = key
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        s = mfma32(rows_frag(Qs, 32 * qb + i32, d, g), kf[d], s);
+        dp = mfma32(rows_frag(Ds, 32 * qb + i32, d, g), vf[d], dp);
+      }
+      // P = 2^(s*c2 - lse2), dS = P (dP - D); register r is query
+      // 32*qb + 8*(r/4) + 4*g + r%4 of the tile
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int ql = 32 * qb + 8 * rg + 4 * g;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(lt + 2 * ql);       // (lse2, D) of queries ql, ql+1
+        const f32x4 bq = *reinterpret_cast<const f32x4*>(lt + 2 * ql + 4);  // ql+2, ql+3
+        const float l2[4] = {a[0], a[2], bq[0], bq[2]};
+        const float dd[4] = {a[1], a[3], bq[1], bq[3]};
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+          const int r = 4 * rg + t4;
+          float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2[t4]));
+          if (need_mask) {
+            const int qi = q0 + ql + t4;
+            const bool legal = kj < Lkv && qi < Lq && (!p.causal || kj <= qi);
+            pr = legal ? pr : 0.f;
+          }
+          pv[r] = pr;
+          dsv[r] = pr * (dp[r] - dd[t4]);
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries of this block
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const bf16x8 pf = pack8(pv + 8 * sb);
+        const bf16x8 sf = pack8(dsv + 8 * sb);
+        dv0 = mfma32(tr_frag(Ds, 0, qb, sb, lane), pf, dv0);
+        dv1 = mfma32(tr_frag(Ds, 1, qb, sb, lane), pf, dv1);
+        dk0 = mfma32(tr_frag(Qs, 0, qb, sb, lane), sf, dk0);
+        dk1 = mfma32(tr_frag(Qs, 1, qb, sb, lane), sf, dk1);
+      }
+    }
+  }
+
+  // dK = scale dK^T, dV = dV^T, one rounding to bf16; register r of block cb
+  // holds d = 32*cb + 8*(r/4) + 4*g + r%4 of key kj
+  if (kj < p.n_kv) {
+    __bf16* dkrow = reinterpret_cast<__bf16*>(p.dk) + b * p.dks_b + h * p.dks_h + (int64_t)kj * p.dks_n;
+    __bf16* dvrow = reinterpret_cast<__bf16*>(p.dv) + b * p.dvs_b + h * p.dvs_h + (int64_t)kj * p.dvs_n;
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      bf16x4 a0, a1, b0, b1;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        a0[t] = (__bf16)(dk0[4 * rg + t] * p.scale);
+        a1[t] = (__bf16)(dk1[4 * rg + t] * p.scale);
+        b0[t] = (__bf16)dv0[4 * rg + t];
+        b1[t] = (__bf16)dv1[4 * rg + t];
+      }
+      *reinterpret_cast<u32x2*>(dkrow + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, a0);
+      *reinterpret_cast<u32x2*>(dkrow + 32 + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, a1);
+      *reinterpret_cast<u32x2*>(dvrow + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, b0);
+      *reinterpret_cast<u32x2*>(dvrow + 32 + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, b1);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int NS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void sdpa_bwd_dq(const SdpaBwdParams p) {
+  constexpr int BM = 128;                  // queries per workgroup (4 waves x 32)
+  constexpr int STAGE_E = 2 * TILE_E;      // K tile, V tile
+  constexpr int IPT = 4;
+  static_assert(NS >= 2 && NS <= 4, "bad configuration");
+  __shared__ __attribute__((aligned(1024))) __bf16 smem[NS * STAGE_E];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i32 = lane & 31, g = lane >> 5;
+  const int bhn = p.batch * p.heads;
+  const int nqb = (p.n_q + BM - 1) / BM;
+  const int qb_idx = blockIdx.x / bhn;
+  const int bh = blockIdx.x - qb_idx * bhn;
+  const int qb = p.causal ? nqb - 1 - qb_idx : qb_idx;   // causal: the longest blocks first
+  const int b = bh / p.heads, h = bh - b * p.heads;
+  int Lq = p.n_q, Lkv = p.n_kv;
+  if (p.seqlens_q) Lq = min(max(p.seqlens_q[b], 0), p.n_q);
+  if (p.seqlens_kv) Lkv = min(max(p.seqlens_kv[b], 0), p.n_kv);
+
+  const int q0 = qb * BM, qw0 = q0 + 32 * wave, qi = qw0 + i32;
+  int kv_end = Lkv, wkv_end = Lkv;
+  if (p.causal) {
+    kv_end = min(kv_end, min(q0 + BM, Lq));
+    wkv_end = min(wkv_end, min(qw0 + 32, Lq));
+  }
+  if (q0 >= Lq) kv_end = 0;
+  if (qw0 >= Lq) wkv_end = 0;
+  const int nblk = (kv_end + BT - 1) / BT;
+
+  // Q and dO fragments of this lane's query (B operands: lane = query, k = d),
+  // its lse2 and D; padded rows read zeros and lse2 = +inf (weights 0)
+  bf16x8 qf[4], df[4];
+  float lse2 = INFINITY, dd = 0.f;
+  {
+    const bool qvalid = qi < Lq;
+    const int ii = qvalid ? qi : 0;
+    const __bf16* qrow = reinterpret_cast<const __bf16*>(p.q) + b * p.qs_b + h * p.qs_h + (int64_t)ii * p.qs_n;
+    const __bf16* drow = reinterpret_cast<const __bf16*>(p.dout) + b * p.dos_b + h * p.dos_h + (int64_t)ii * p.dos_n;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(qrow + 16 * d + 8 * g);
+      const bf16x8 c = *reinterpret_cast<const bf16x8*>(drow + 16 * d + 8 * g);
+      qf[d] = qvalid ? a : bf16x8{};
+      df[d] = qvalid ? c : bf16x8{};
+    }
+    const f32x2 l = *reinterpret_cast<const f32x2*>(p.ld + 2 * ((int64_t)bh * p.n_q + ii));
+    if (qvalid) {
+      lse2 = l[0];
+      dd = l[1];
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) asm volatile("" ::"v"(qf[d]), "v"(df[d]));
+    asm volatile("" ::"v"(lse2), "v"(dd));
+  }
+
+  const __bf16* Kb = reinterpret_cast<const __bf16*>(p.k) + b * p.ks_b + h * p.ks_h;
+  const __bf16* Vb = reinterpret_cast<const __bf16*>(p.v) + b * p.vs_b + h * p.vs_h;
+  const uint32_t k_bytes = Lkv > 0 ? (uint32_t)((int64_t)(Lkv - 1) * p.ks_n * 2 + 128) : 0u;
+  const uint32_t v_bytes = Lkv > 0 ? (uint32_t)((int64_t)(Lkv - 1) * p.vs_n * 2 + 128) : 0u;
+  uint32_t dma_off[IPT];
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const int u = wave * IPT + i;
+    const bool is_v = u >= 8;
+    const int r = 8 * (u & 7) + (lane >> 3);
+    const int c = (lane & 7) ^ swz_k(r);
+    dma_off[i] = (uint32_t)(((int64_t)r * (is_v ? p.vs_n : p.ks_n) + c * 8) * 2);
+  }
+  auto issue_tile = [&](int t) {
+    const int64_t k_adv = (int64_t)t * BT * p.ks_n, v_adv = (int64_t)t * BT * p.vs_n;
+    const i32x4 rk = make_rsrc(Kb + k_adv, (uint32_t)max<int64_t>(0, (int64_t)k_bytes - 2 * k_adv));
+    const i32x4 rv = make_rsrc(Vb + v_adv, (uint32_t)max<int64_t>(0, (int64_t)v_bytes - 2 * v_adv));
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int u = wave * IPT + i;
+      const bool is_v = u >= 8;
+      const __bf16* dst = smem + (t % NS) * STAGE_E + (is_v ? TILE_E : 0) + (u & 7) * 512;
+      dma16(dma_off[i], is_v ? rv : rk, lds_addr(dst));
+    }
+  };
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < nblk) issue_tile(t);
+
+  f32x16 dq0 = {}, dq1 = {};   // dQ^T for d 0..31 / 32..63, lane = query
+  const float c2 = p.scale_log2;
+  constexpr int kFar = 1 << 30;
+  for (int blk = 0; blk < nblk; ++blk) {
+    wait_vmcnt_le<IPT>(min(NS - 2, nblk - 1 - blk) * IPT);
+    barrier_lds();
+    if (blk + NS - 1 < nblk) issue_tile(blk + NS - 1);
+    const int key0 = blk * BT;
+    if (key0 >= wkv_end) continue;
+    const __bf16* Ks = smem + (blk % NS) * STAGE_E;
+    const __bf16* Vs = Ks + TILE_E;
+    // S^T = K Q^T and dP^T = V dO^T: sc/dp[jb] for keys 32*jb..; register r is
+    // key key0 + 32*jb + 8*(r/4) + 4*g + r%4, lane column the query qi
+    f32x16 sc[2] = {}, dp[2] = {};
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        sc[jb] = mfma32(rows_frag(Ks, 32 * jb + i32, d, g), qf[d], sc[jb]);
+        dp[jb] = mfma32(rows_frag(Vs, 32 * jb + i32, d, g), df[d], dp[jb]);
+      }
+    const bool need_mask = key0 + BT > Lkv || (p.causal && key0 + BT - 1 > qw0);
+    const int lim = min(Lkv - 1, p.causal ? qi : kFar);
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+      float dsv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = __builtin_amdgcn_exp2f(fmaf(sc[jb][r], c2, -lse2));
+        if (need_mask) {
+          const int key = key0 + 32 * jb + 8 * (r >> 2) + 4 * g + (r & 3);
+          pr = key <= lim ? pr : 0.f;
+        }
+        dsv[r] = pr * (dp[jb][r] - dd);
+      }
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const bf16x8 sf = pack8(dsv + 8 * sb);
+        dq0 = mfma32(tr_frag(Ks, 0, jb, sb, lane), sf, dq0);
+        dq1 = mfma32(tr_frag(Ks, 1, jb, sb, lane), sf, dq1);
+      }
+    }
+  }
+
+  // dQ = scale dQ^T, one rounding to bf16 (rows past the length are zeros)
+  if (qi < p.n_q) {
+    __bf16* dqrow = reinterpret_cast<__bf16*>(p.dq) + b * p.dqs_b + h * p.dqs_h + (int64_t)qi * p.dqs_n;
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      bf16x4 a0, a1;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        a0[t] = (__bf16)(dq0[4 * rg + t] * p.scale);
+        a1[t] = (__bf16)(dq1[4 * rg + t] * p.scale);
+      }
+      *reinterpret_cast<u32x2*>(dqrow + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, a0);
+      *reinterpret_cast<u32x2*>(dqrow + 32 + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, a1);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_sdpa_bwd_bf16(const SdpaBwdParams& p, hipStream_t stream) {
+  const int64_t bh = (int64_t)p.batch * p.heads;
+  if (bh == 0) return hipSuccess;
+  if (p.n_q > 0) {
+    const int64_t rows = bh * p.n_q;
+    hipLaunchKernelGGL(sdpa_bwd_pre, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.n_kv > 0) {
+    const int64_t grid = (int64_t)((p.n_kv + 127) / 128) * bh;
+    hipLaunchKernelGGL(sdpa_bwd_dkdv<2>, dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.n_q > 0) {
+    const int64_t grid = (int64_t)((p.n_q + 127) / 128) * bh;
+    hipLaunchKernelGGL(sdpa_bwd_dq<2>, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace attn

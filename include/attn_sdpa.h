@@ -26,6 +26,12 @@
  *   attn_linear_fwd one projection of that block on its own, Y = X.W (the
  *                  products X W_i^Q, X W_i^K, X W_i^V and Concat(...) W^O of
  *                  section 3.2.2; rockcohen.cc 5.2).
+ *   attn_sdpa_bwd  gradients of Eq. 1 with respect to Q, K and V for a given
+ *                  gradient of O (the model is trained end to end: the
+ *                  vlmlib.cn summary's training-objective paragraph;
+ *                  attention-paper-guide section 05), from the chain rule
+ *                  through the softmax, recomputing the weights from the
+ *                  forward's lse.
  *
  * Masking.  Key j is legal for query i iff j < L_kv[b] (when key lengths are
  * given) and, with ATTN_MASK_CAUSAL, j <= i (the decoder's illegal
@@ -58,7 +64,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 typedef void* attn_stream_t; /* hipStream_t */
 
@@ -222,6 +228,49 @@ int attn_decode_fwd(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int 
  */
 int attn_linear_fwd(attn_dtype dt, int m, int k, int n, const void* x, int64_t ldx, const void* w,
                     void* y, int64_t ldy, attn_stream_t stream);
+
+/*
+ * attn_sdpa_bwd_workspace_bytes -- workspace attn_sdpa_bwd needs for these
+ * sizes (batch*heads*n_q*8 bytes rounded up to 256), or 0 when they are
+ * invalid or unsupported.
+ */
+size_t attn_sdpa_bwd_workspace_bytes(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k,
+                                     int d_v);
+
+/*
+ * attn_sdpa_bwd -- gradients of scaled dot-product attention.
+ *
+ * For a loss with gradient dO at the output of attn_sdpa_fwd (same q, k, v,
+ * scale, mask and lengths), writes, per (batch, head), with P the forward's
+ * weights and D_i = sum_c dO_ic O_ic:
+ *   dV = P^T dO,   dS = P * (dO V^T - D),   dQ = scale dS K,   dK = scale dS^T Q.
+ * P is recomputed as exp(scale q_i.k_j - lse_i), so o and lse must be the
+ * outputs of that forward call.  Gradients of padded query rows (i >= L_q),
+ * of rows with no legal key and of keys no query may use (j >= L_kv) are
+ * written as zeros.
+ *
+ *   q, k, v, o, dout, dq, dk, dv   bf16 [batch, heads, n, 64], strides as for
+ *               attn_sdpa_fwd (NULL = contiguous): sq for q, sk for k, sv
+ *               for v, so for o, sdo for dout, sdq for dq, sdk for dk, sdv
+ *               for dv.  Same alignment and size rules as attn_sdpa_fwd.
+ *   lse         device fp32 [batch*heads*n_q], the forward's lse (required).
+ *   dt          ATTN_BF16 only (ATTN_F32 gives ATTN_E_UNSUPPORTED): products
+ *               accumulate in fp32, P and dS are rounded to bf16 for the
+ *               products that consume them, dQ, dK, dV once to bf16.
+ *   workspace   device memory of attn_sdpa_bwd_workspace_bytes(...) bytes,
+ *               256-byte aligned; contents on entry are ignored.
+ * dq, dk, dv are overwritten (not accumulated into) and must not overlap each
+ * other, the inputs or the workspace.  Returns ATTN_OK or a negative
+ * attn_status; nothing is enqueued on error.
+ */
+int attn_sdpa_bwd(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k, int d_v,
+                  const void* q, const attn_strides* sq, const void* k, const attn_strides* sk,
+                  const void* v, const attn_strides* sv, const void* o, const attn_strides* so,
+                  const void* dout, const attn_strides* sdo, const float* lse, void* dq,
+                  const attn_strides* sdq, void* dk, const attn_strides* sdk, void* dv,
+                  const attn_strides* sdv, float scale, attn_mask mask, const int32_t* seqlens_q,
+                  const int32_t* seqlens_kv, void* workspace, size_t workspace_bytes,
+                  attn_stream_t stream);
 
 /* ATTN_ABI_VERSION of the loaded library. */
 int attn_abi_version(void);

@@ -181,3 +181,50 @@ def test_sdpa_window_validation():
     assert L.attn_sdpa_window_fwd(*args, -1, None, None, None, None) == -1          # negative radius
     assert L.attn_sdpa_window_fwd(1, 1, 1, 128, 128, 32, 32, *args[7:], 4, None, None, None, None) == -2
     assert L.attn_sdpa_window_fwd(*args[:7], MISALIGNED, *args[8:], 4, None, None, None, None) == -3
+
+
+def bwd_call(dt=1, B=2, H=2, nq=100, nkv=100, dk=64, dv=64, q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE,
+             lse=FAKE, dq=FAKE, dk_=FAKE, dv_=FAKE, sdo=None, mask=1, ws=FAKE, wsb=1 << 30, scale=0.0):
+    return attn.lib().attn_sdpa_bwd(dt, B, H, nq, nkv, dk, dv, q, None, k, None, v, None, o, None,
+                                    do, sdo, lse, dq, None, dk_, None, dv_, None, scale, mask, None, None,
+                                    ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), -1),
+    (dict(B=0), -1),
+    (dict(nq=-1), -1),
+    (dict(mask=2), -1),
+    (dict(q=None), -1),
+    (dict(do=None), -1),
+    (dict(lse=None), -1),
+    (dict(dq=None), -1),
+    (dict(dk_=None), -1),
+    (dict(dv_=None), -1),
+    (dict(scale=float("nan")), -1),
+    (dict(sdo=attn.attn_strides(-1, 64, 64)), -1),
+    (dict(dt=0), -2),
+    (dict(dk=32, dv=32), -2),
+    (dict(sdo=attn.attn_strides(64 * 100, 64 * 100, 32)), -2),  # dO rows overlap
+    (dict(do=MISALIGNED), -3),
+    (dict(dv_=MISALIGNED), -3),
+    (dict(lse=FAKE + 2), -3),
+    (dict(sdo=attn.attn_strides(64 * 100, 64 * 100, 68)), -3),
+    (dict(ws=FAKE + 64), -3),
+    (dict(ws=None), -4),
+    (dict(wsb=2 * 2 * 100 * 8 - 1), -4),
+    (dict(nq=0, nkv=0, q=None, k=None, v=None, o=None, do=None, lse=None, dq=None, dk_=None, dv_=None,
+          ws=None, wsb=0), 0),   # nothing to do: no launch
+])
+def test_bwd_validation(kw, code):
+    assert bwd_call(**kw) == code
+
+
+def test_bwd_workspace_bytes():
+    L = attn.lib()
+    # one (lse in log2 units, D) fp32 pair per query row, rounded up to 256 bytes
+    assert L.attn_sdpa_bwd_workspace_bytes(1, 4, 16, 4096, 4096, 64, 64) == 4 * 16 * 4096 * 8
+    assert L.attn_sdpa_bwd_workspace_bytes(1, 1, 1, 3, 5, 64, 64) == 256
+    assert L.attn_sdpa_bwd_workspace_bytes(1, 1, 1, 0, 5, 64, 64) == 0
+    assert L.attn_sdpa_bwd_workspace_bytes(0, 1, 1, 3, 5, 64, 64) == 0      # f32 unsupported
+    assert L.attn_sdpa_bwd_workspace_bytes(1, 1, 1, 3, 5, 32, 32) == 0
