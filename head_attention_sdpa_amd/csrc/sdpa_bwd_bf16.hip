@@ -44,17 +44,25 @@ constexpr int BT = 64;         // rows per streamed tile (queries or keys)
 constexpr int TILE_E = BT * D; // bf16 elements of one [64][64] tile (8 KiB)
 constexpr float LOG2E = 1.4426950408889634f;
 
+// Tiles here are read both ways: as rows (one 16-byte chunk of 32 consecutive
+// rows per half-wave) and transposed (8 rows x 64 bytes per ds_read_b64_tr_b16).
+// The 16-byte chunk c of row r sits at chunk position c ^ swz_qt(r); bits 0-1
+// of the swizzle spread 8 consecutive rows' chunk over distinct bank groups
+// for the row reads, bit 2 moves rows 4m+2, 4m+3 to the other half of the
+// banks, which the transposed reads need.
+__device__ __forceinline__ int swz_qt(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+
 // A [32 x 16] operand (rows r0 + lane%32, columns 16*dstep + 8*g + 0..7) read
-// from a row-major [64][64] tile stored with the swz_k chunk swizzle.
+// from a row-major [64][64] tile.
 __device__ __forceinline__ bf16x8 rows_frag(const __bf16* tile, int r, int dstep, int g) {
   const int c = 2 * dstep + g;
-  return *reinterpret_cast<const bf16x8*>(tile + r * D + 8 * (c ^ swz_k(r)));
+  return *reinterpret_cast<const bf16x8*>(tile + r * D + 8 * (c ^ swz_qt(r)));
 }
 
 // The transposed operand of block (cb, jb, s): element t of lane l is
 // tile[row(t)][32*cb + l%32] with row(t) = 32*jb + 16*s + 8*(t/4) + 4*g + t%4,
 // the row order of the score accumulator's C layout, read with two
-// ds_read_b64_tr_b16 from the swz_k-swizzled tile.
+// ds_read_b64_tr_b16.
 __device__ __forceinline__ bf16x8 tr_frag(const __bf16* tile, int cb, int jb, int s, int lane) {
   const int k16 = lane & 15, g = lane >> 5;
   const int chalf = (lane >> 4) & 1;
@@ -65,7 +73,7 @@ __device__ __forceinline__ bf16x8 tr_frag(const __bf16* tile, int cb, int jb, in
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
     const int row = 32 * jb + 16 * s + 8 * hh + tr_row;
-    part[hh] = tr_read(tile + row * D + tr_half + 8 * ((4 * cb + tr_chunk) ^ swz_k(row)));
+    part[hh] = tr_read(tile + row * D + tr_half + 8 * ((4 * cb + tr_chunk) ^ swz_qt(row)));
   }
   return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
 }
@@ -113,7 +121,7 @@ __global__ __launch_bounds__(256) void sdpa_bwd_pre(const SdpaBwdParams p) {
 
 // ---------------------------------------------------------------------------
 template <int NS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void sdpa_bwd_dkdv(const SdpaBwdParams p) {
   constexpr int BK = 128;                  // keys per workgroup (4 waves x 32)
   constexpr int STAGE_E = 2 * TILE_E;      // Q tile, dO tile
@@ -176,7 +184,7 @@ void sdpa_bwd_dkdv(const SdpaBwdParams p) {
     const int u = wave * 4 + i;
     const bool is_o = u >= 8;
     const int r = 8 * (u & 7) + (lane >> 3);
-    const int c = (lane & 7) ^ swz_k(r);
+    const int c = (lane & 7) ^ swz_qt(r);
     dma_off[i] = (uint32_t)(((int64_t)r * (is_o ? p.dos_n : p.qs_n) + c * 8) * 2);
   }
   auto issue_stage = [&](int j) {
@@ -211,7 +219,12 @@ void sdpa_bwd_dkdv(const SdpaBwdParams p) {
     const __bf16* Qs = smem + (t % NS) * STAGE_E;
     const __bf16* Ds = Qs + TILE_E;
     const float* lt = &lds_ld[t % NS][wave][0];
-    const bool need_mask = (p.causal && q0 < kw0 + 32) || q0 + BT > Lq || kw0 + 32 > Lkv;
+    // Only the causal mask needs applying: rows past L_q have lse2 = +inf
+    // (weight 0), rows past n_q and keys past L_kv read as zeros, so their dS
+    // and dO are 0 and they add nothing to the legal keys' columns; the
+    // columns of keys past L_kv are replaced by zeros at the store.
+    const bool diag = p.causal && q0 < kw0 + 32;
+    const int qlo = kj - q0 - 4 * g;   // legal: query offset (in the tile, less 4*g) >= qlo
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       // S = Q K^T and dP = dO V^T for queries q0 + 32*qb + row(r): lane = key
@@ -221,8 +234,13 @@ void sdpa_bwd_dkdv(const SdpaBwdParams p) {
         s = mfma32(rows_frag(Qs, 32 * qb + i32, d, g), kf[d], s);
         dp = mfma32(rows_frag(Ds, 32 * qb + i32, d, g), vf[d], dp);
       }
-      // P = 2^(s*c2 - lse2), dS = P (dP - D); register r is query
-      // 32*qb + 8*(r/4) + 4*g + r%4 of the tile
+      // register r is query 32*qb + 8*(r/4) + 4*g + r%4 of the tile
+      if (diag) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * qb + 8 * (r >> 2) + (r & 3) < qlo) s[r] = -INFINITY;
+      }
+      // P = 2^(s*c2 - lse2), dS = P (dP - D)
       float pv[16], dsv[16];
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
@@ -234,12 +252,7 @@ void sdpa_bwd_dkdv(const SdpaBwdParams p) {
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) {
           const int r = 4 * rg + t4;
-          float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2[t4]));
-          if (need_mask) {
-            const int qi = q0 + ql + t4;
-            const bool legal = kj < Lkv && qi < Lq && (!p.causal || kj <= qi);
-            pr = legal ? pr : 0.f;
-          }
+          const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2[t4]));
           pv[r] = pr;
           dsv[r] = pr * (dp[r] - dd[t4]);
         }
@@ -260,6 +273,7 @@ void sdpa_bwd_dkdv(const SdpaBwdParams p) {
   // dK = scale dK^T, dV = dV^T, one rounding to bf16; register r of block cb
   // holds d = 32*cb + 8*(r/4) + 4*g + r%4 of key kj
   if (kj < p.n_kv) {
+    const bool kvalid = kj < Lkv;   // the columns of keys past L_kv hold no gradient (maybe inf/NaN)
     __bf16* dkrow = reinterpret_cast<__bf16*>(p.dk) + b * p.dks_b + h * p.dks_h + (int64_t)kj * p.dks_n;
     __bf16* dvrow = reinterpret_cast<__bf16*>(p.dv) + b * p.dvs_b + h * p.dvs_h + (int64_t)kj * p.dvs_n;
 #pragma unroll
@@ -267,10 +281,10 @@ void sdpa_bwd_dkdv(const SdpaBwdParams p) {
       bf16x4 a0, a1, b0, b1;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        a0[t] = (__bf16)(dk0[4 * rg + t] * p.scale);
-        a1[t] = (__bf16)(dk1[4 * rg + t] * p.scale);
-        b0[t] = (__bf16)dv0[4 * rg + t];
-        b1[t] = (__bf16)dv1[4 * rg + t];
+        a0[t] = (__bf16)(kvalid ? dk0[4 * rg + t] * p.scale : 0.f);
+        a1[t] = (__bf16)(kvalid ? dk1[4 * rg + t] * p.scale : 0.f);
+        b0[t] = (__bf16)(kvalid ? dv0[4 * rg + t] : 0.f);
+        b1[t] = (__bf16)(kvalid ? dv1[4 * rg + t] : 0.f);
       }
       *reinterpret_cast<u32x2*>(dkrow + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, a0);
       *reinterpret_cast<u32x2*>(dkrow + 32 + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, a1);
@@ -282,7 +296,7 @@ void sdpa_bwd_dkdv(const SdpaBwdParams p) {
 
 // ---------------------------------------------------------------------------
 template <int NS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void sdpa_bwd_dq(const SdpaBwdParams p) {
   constexpr int BM = 128;                  // queries per workgroup (4 waves x 32)
   constexpr int STAGE_E = 2 * TILE_E;      // K tile, V tile
@@ -349,7 +363,7 @@ void sdpa_bwd_dq(const SdpaBwdParams p) {
     const int u = wave * IPT + i;
     const bool is_v = u >= 8;
     const int r = 8 * (u & 7) + (lane >> 3);
-    const int c = (lane & 7) ^ swz_k(r);
+    const int c = (lane & 7) ^ swz_qt(r);
     dma_off[i] = (uint32_t)(((int64_t)r * (is_v ? p.vs_n : p.ks_n) + c * 8) * 2);
   }
   auto issue_tile = [&](int t) {
@@ -389,18 +403,22 @@ void sdpa_bwd_dq(const SdpaBwdParams p) {
         sc[jb] = mfma32(rows_frag(Ks, 32 * jb + i32, d, g), qf[d], sc[jb]);
         dp[jb] = mfma32(rows_frag(Vs, 32 * jb + i32, d, g), df[d], dp[jb]);
       }
-    const bool need_mask = key0 + BT > Lkv || (p.causal && key0 + BT - 1 > qw0);
-    const int lim = min(Lkv - 1, p.causal ? qi : kFar);
+    // keys past this lane's query (causal) or past L_kv get score -inf, so
+    // weight 0 and dS 0 (rows past L_q already have lse2 = +inf)
+    if (key0 + BT > Lkv || (p.causal && key0 + BT - 1 > qw0)) {
+      const int krel = min(Lkv - 1, p.causal ? qi : kFar) - key0 - 4 * g;   // legal: offset <= krel
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * jb + 8 * (r >> 2) + (r & 3) > krel) sc[jb][r] = -INFINITY;
+    }
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
       float dsv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(fmaf(sc[jb][r], c2, -lse2));
-        if (need_mask) {
-          const int key = key0 + 32 * jb + 8 * (r >> 2) + 4 * g + (r & 3);
-          pr = key <= lim ? pr : 0.f;
-        }
+        const float pr = __builtin_amdgcn_exp2f(fmaf(sc[jb][r], c2, -lse2));
         dsv[r] = pr * (dp[jb][r] - dd);
       }
 #pragma unroll
