@@ -60,11 +60,18 @@ def _load():
         lib.oracle_sdpa_window_f64.argtypes = [i, i, i, i, i, i, _D, _D, _D, _D, _D, d, i, _I, _I, i, i]
         lib.oracle_decode_f64.argtypes = [i, i, i, i, i, i, _D, _D, _D, _D, _D, d, _I, i]
         lib.oracle_linear_f64.argtypes = [i, i, i, _D, ctypes.c_int64, _L, ctypes.c_int64, _D, _D, i]
+        lib.oracle_pe_f64.argtypes = [i, i, _D]
+        lib.oracle_layernorm_f64.argtypes = [ctypes.c_int64, i, _D, _D, _D, d, _D]
+        lib.oracle_mha_block_f64.argtypes = [i, i, i, i, i, i, i, _D, _D, i, _D, _D, _D, _D, _D, _D, d,
+                                             _D, _D, d, i, _I, _I, i]
+        lib.oracle_mha_block_rows_f64.argtypes = [i, i, i, i, i, i, i, _D, _D, i, _D, _D, _D, _D, _D,
+                                                  _D, d, _L, ctypes.c_int64, _D, _D, d, i, _I, _I, i]
         lib.oracle_round_bf16.argtypes = [d]
         lib.oracle_round_bf16.restype = d
         for f in ("oracle_sdpa_f64", "oracle_sdpa_rows_f64", "oracle_mha_f64", "oracle_mha_rows_f64",
                   "oracle_linear_f64", "oracle_decode_f64", "oracle_sdpa_window_f64",
-                  "oracle_sdpa_bwd_f64"):
+                  "oracle_sdpa_bwd_f64", "oracle_pe_f64", "oracle_layernorm_f64",
+                  "oracle_mha_block_f64", "oracle_mha_block_rows_f64"):
             getattr(lib, f).restype = i
         _lib = lib
     return _lib
@@ -263,6 +270,89 @@ def linear(x, w, rows=None, nthreads=None):
                                    nthreads or default_threads())
     _check(rc, "oracle_linear_f64")
     return y
+
+
+def positional_encoding(n, d_model):
+    """Sinusoidal positional encoding [n, d_model] in fp64: sin on even and cos
+    on odd columns of pos / 10000^(2i/d_model) (paper section 3.5)."""
+    pe = np.empty((n, d_model))
+    _check(_load().oracle_pe_f64(n, d_model, _ptr(pe)), "oracle_pe_f64")
+    return pe
+
+
+def layernorm(z, gamma, beta, eps):
+    """LayerNorm over the last dimension in fp64 (population variance, eps
+    inside the square root), then the gain gamma and bias beta."""
+    z = _f64(z)
+    d = z.shape[-1]
+    gamma, beta = _f64(gamma), _f64(beta)
+    if gamma.shape != (d,) or beta.shape != (d,):
+        raise ValueError("gamma and beta must have shape [d]")
+    y = np.empty_like(z)
+    _check(_load().oracle_layernorm_f64(z.size // d, d, _ptr(z), _ptr(gamma), _ptr(beta), float(eps),
+                                        _ptr(y)), "oracle_layernorm_f64")
+    return y
+
+
+def _block_args(x_q, x_kv, w_q, w_k, w_v, w_o, gamma, beta, heads):
+    x_q = _f64(x_q)
+    x_kv = None if x_kv is None else _f64(x_kv)
+    w_q, w_k, w_v, w_o = _f64(w_q), _f64(w_k), _f64(w_v), _f64(w_o)
+    gamma, beta = _f64(gamma), _f64(beta)
+    B, n_q, d_model = x_q.shape
+    n_kv = n_q if x_kv is None else x_kv.shape[1]
+    d_k = w_q.shape[1] // heads
+    d_v = w_v.shape[1] // heads
+    if (w_q.shape != (d_model, heads * d_k) or w_k.shape != w_q.shape
+            or w_v.shape != (d_model, heads * d_v) or w_o.shape != (heads * d_v, d_model)
+            or (x_kv is not None and x_kv.shape != (B, n_kv, d_model))
+            or gamma.shape != (d_model,) or beta.shape != (d_model,)):
+        raise ValueError("shape mismatch")
+    return x_q, x_kv, w_q, w_k, w_v, w_o, gamma, beta, B, n_q, n_kv, d_model, d_k, d_v
+
+
+def mha_block(x_q, w_q, w_k, w_v, w_o, gamma, beta, heads, x_kv=None, add_pe=False, eps=1e-5,
+              scale=None, causal=False, seqlens_q=None, seqlens_kv=None, nthreads=None):
+    """The attention sublayer in fp64: h = x_q (+ PE), z = h + MultiHead(h,
+    kv, kv) with kv = h (x_kv None: self-attention) or x_kv (cross-attention,
+    no PE), y = LayerNorm(z) with gain gamma and bias beta.  Returns (y, z),
+    both [B, n_q, d_model]."""
+    (x_q, x_kv, w_q, w_k, w_v, w_o, gamma, beta, B, n_q, n_kv, d_model, d_k,
+     d_v) = _block_args(x_q, x_kv, w_q, w_k, w_v, w_o, gamma, beta, heads)
+    scale = 1.0 / math.sqrt(d_k) if scale is None else float(scale)
+    y = np.empty((B, n_q, d_model))
+    z = np.empty((B, n_q, d_model))
+    lq, plq = _lens(seqlens_q, B)
+    lk, plk = _lens(seqlens_kv, B)
+    rc = _load().oracle_mha_block_f64(B, n_q, n_kv, d_model, heads, d_k, d_v, _ptr(x_q),
+                                      None if x_kv is None else _ptr(x_kv), int(bool(add_pe)),
+                                      _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_o), _ptr(gamma),
+                                      _ptr(beta), float(eps), _ptr(y), _ptr(z), scale,
+                                      int(bool(causal)), plq, plk, nthreads or default_threads())
+    _check(rc, "oracle_mha_block_f64")
+    return y, z
+
+
+def mha_block_rows(x_q, w_q, w_k, w_v, w_o, gamma, beta, heads, rows, x_kv=None, add_pe=False,
+                   eps=1e-5, scale=None, causal=False, seqlens_q=None, seqlens_kv=None, nthreads=None):
+    """mha_block for selected output rows only (flat indices b*n_q + i).
+    Returns (y, z), each [len(rows), d_model]."""
+    (x_q, x_kv, w_q, w_k, w_v, w_o, gamma, beta, B, n_q, n_kv, d_model, d_k,
+     d_v) = _block_args(x_q, x_kv, w_q, w_k, w_v, w_o, gamma, beta, heads)
+    scale = 1.0 / math.sqrt(d_k) if scale is None else float(scale)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    y = np.empty((len(rows), d_model))
+    z = np.empty((len(rows), d_model))
+    lq, plq = _lens(seqlens_q, B)
+    lk, plk = _lens(seqlens_kv, B)
+    rc = _load().oracle_mha_block_rows_f64(B, n_q, n_kv, d_model, heads, d_k, d_v, _ptr(x_q),
+                                           None if x_kv is None else _ptr(x_kv), int(bool(add_pe)),
+                                           _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_o), _ptr(gamma),
+                                           _ptr(beta), float(eps), rows.ctypes.data_as(_L), len(rows),
+                                           _ptr(y), _ptr(z), scale, int(bool(causal)), plq, plk,
+                                           nthreads or default_threads())
+    _check(rc, "oracle_mha_block_rows_f64")
+    return y, z
 
 
 def round_bf16(x: float) -> float:

@@ -14,8 +14,10 @@
  *   (3) one projection of that block, y = x . W (no bias), and
  *   (4) one decoding step over a key/value cache (the newest n_q positions of
  *       each sequence under the causal mask),
- *   (5) restricted self-attention over a neighbourhood of radius r, and
- *   (6) the gradients of SDPA with respect to Q, K and V.
+ *   (5) restricted self-attention over a neighbourhood of radius r,
+ *   (6) the gradients of SDPA with respect to Q, K and V, and
+ *   (7) the attention sublayer around the MHA: sinusoidal positional encoding
+ *       added to the input, then LayerNorm(x + MultiHead(x, ...)).
  *
  * Definitions followed literally, one query row at a time:
  *   legal(j)  <=>  j < n_kv  and  (no key lengths or j < L_kv[b])
@@ -501,6 +503,122 @@ int oracle_mha_rows_f64(int B, int n_q, int n_kv, int d_model, int H, int d_k, i
     }
   }
   free(kp); free(vp); free(qp); free(oc); free(sel); free(xrow);
+  return rc;
+}
+
+/* ---- Positional encoding, LayerNorm, the attention sublayer -------------- */
+/* Sinusoidal positional encoding (paper section 3.5, restated on the
+ * vlmlib.cn summary and rockcohen.cc section 5.4):
+ *   PE[pos][2i]   = sin(pos / 10000^(2i/d_model))
+ *   PE[pos][2i+1] = cos(pos / 10000^(2i/d_model))
+ * pos counts from 0; for odd d_model the last column is a sine. */
+int oracle_pe_f64(int n, int d_model, double* pe) {
+  if (n < 0 || d_model < 1) return ORACLE_EINVAL;
+  for (int pos = 0; pos < n; ++pos)
+    for (int c = 0; c < d_model; ++c) {
+      int i2 = c - (c & 1);                                   /* 2i */
+      double angle = (double)pos / pow(10000.0, (double)i2 / (double)d_model);
+      pe[(int64_t)pos * d_model + c] = (c & 1) ? cos(angle) : sin(angle);
+    }
+  return ORACLE_OK;
+}
+
+/* LayerNorm over the last dimension (the ai-master transformer_lab page, its
+ * section on the other core components: LN(x) = gamma (x - mu) / sqrt(var +
+ * eps) + beta, with mu and var the mean and the (population) variance of the
+ * d features of one position; rockcohen.cc section 5.5).  Two passes per row:
+ * the mean, then the mean of squared deviations. */
+int oracle_layernorm_f64(int64_t rows, int d, const double* z, const double* gamma,
+                         const double* beta, double eps, double* y) {
+  if (rows < 0 || d < 1 || !(eps >= 0.0)) return ORACLE_EINVAL;
+  for (int64_t r = 0; r < rows; ++r) {
+    const double* zr = z + r * d;
+    double mu = 0.0, var = 0.0;
+    for (int c = 0; c < d; ++c) mu += zr[c];
+    mu /= d;
+    for (int c = 0; c < d; ++c) var += (zr[c] - mu) * (zr[c] - mu);
+    var /= d;
+    double rstd = 1.0 / sqrt(var + eps);
+    for (int c = 0; c < d; ++c) y[r * d + c] = gamma[c] * (zr[c] - mu) * rstd + beta[c];
+  }
+  return ORACLE_OK;
+}
+
+/* The attention sublayer of the encoder and decoder (paper section 3.1, post-LN:
+ * the vlmlib.cn summary's formula Sublayer_out(x) = LayerNorm(x + Sublayer(x));
+ * rockcohen.cc section 5.5):
+ *   h = x_q + PE          (add_pe; the embedding layer's input to the first
+ *                          layer, paper section 3.5; self-attention only)
+ *   z = h + MultiHead(h, kv, kv),  kv = h for self-attention (x_kv == NULL),
+ *                                  else x_kv (cross-attention, no PE)
+ *   y = LayerNorm(z)
+ * All in fp64, no rounding.  z_out (optional) receives z. */
+static int block_prologue(int B, int n_q, int d_model, const double* x_q, int add_pe, double** h_out) {
+  int64_t nh = (int64_t)B * n_q * d_model;
+  double* h = (double*)malloc(sizeof(double) * (size_t)(nh + 1));
+  double* pe = (double*)malloc(sizeof(double) * (size_t)((int64_t)n_q * d_model + 1));
+  if (!h || !pe) { free(h); free(pe); return ORACLE_ENOMEM; }
+  oracle_pe_f64(n_q, d_model, pe);
+  for (int b = 0; b < B; ++b)
+    for (int64_t t = 0; t < (int64_t)n_q * d_model; ++t)
+      h[(int64_t)b * n_q * d_model + t] = x_q[(int64_t)b * n_q * d_model + t] + (add_pe ? pe[t] : 0.0);
+  free(pe);
+  *h_out = h;
+  return ORACLE_OK;
+}
+
+int oracle_mha_block_f64(int B, int n_q, int n_kv, int d_model, int H, int d_k, int d_v,
+                         const double* x_q, const double* x_kv, int add_pe, const double* w_q,
+                         const double* w_k, const double* w_v, const double* w_o,
+                         const double* gamma, const double* beta, double eps, double* y,
+                         double* z_out, double scale, int causal, const int* seqlens_q,
+                         const int* seqlens_kv, int nthreads) {
+  if (add_pe && x_kv) return ORACLE_EINVAL;
+  if (!x_kv && n_kv != n_q) return ORACLE_EINVAL;
+  double* h = NULL;
+  int rc = block_prologue(B, n_q, d_model, x_q, add_pe, &h);
+  if (rc) return rc;
+  int64_t nz = (int64_t)B * n_q * d_model;
+  double* z = (double*)malloc(sizeof(double) * (size_t)(nz + 1));
+  if (!z) { free(h); return ORACLE_ENOMEM; }
+  rc = oracle_mha_f64(B, n_q, n_kv, d_model, H, d_k, d_v, h, x_kv ? x_kv : h, w_q, w_k, w_v, w_o, z,
+                      scale, causal, seqlens_q, seqlens_kv, 0, nthreads);
+  if (!rc) {
+    for (int64_t t = 0; t < nz; ++t) z[t] += h[t];               /* residual */
+    rc = oracle_layernorm_f64((int64_t)B * n_q, d_model, z, gamma, beta, eps, y);
+    if (!rc && z_out) memcpy(z_out, z, sizeof(double) * (size_t)nz);
+  }
+  free(h); free(z);
+  return rc;
+}
+
+/* The same sublayer for selected output rows only (rows[r] = b*n_q + i; y and
+ * z_out are [nrows, d_model]). */
+int oracle_mha_block_rows_f64(int B, int n_q, int n_kv, int d_model, int H, int d_k, int d_v,
+                              const double* x_q, const double* x_kv, int add_pe, const double* w_q,
+                              const double* w_k, const double* w_v, const double* w_o,
+                              const double* gamma, const double* beta, double eps,
+                              const int64_t* rows, int64_t nrows, double* y, double* z_out,
+                              double scale, int causal, const int* seqlens_q, const int* seqlens_kv,
+                              int nthreads) {
+  if (add_pe && x_kv) return ORACLE_EINVAL;
+  if (!x_kv && n_kv != n_q) return ORACLE_EINVAL;
+  for (int64_t r = 0; r < nrows; ++r)
+    if (rows[r] < 0 || rows[r] >= (int64_t)B * n_q) return ORACLE_EINVAL;
+  double* h = NULL;
+  int rc = block_prologue(B, n_q, d_model, x_q, add_pe, &h);
+  if (rc) return rc;
+  double* z = (double*)malloc(sizeof(double) * (size_t)(nrows * d_model + 1));
+  if (!z) { free(h); return ORACLE_ENOMEM; }
+  rc = oracle_mha_rows_f64(B, n_q, n_kv, d_model, H, d_k, d_v, h, x_kv ? x_kv : h, w_q, w_k, w_v, w_o,
+                           rows, nrows, z, scale, causal, seqlens_q, seqlens_kv, 0, nthreads);
+  if (!rc) {
+    for (int64_t r = 0; r < nrows; ++r)
+      for (int c = 0; c < d_model; ++c) z[r * d_model + c] += h[rows[r] * d_model + c];
+    rc = oracle_layernorm_f64(nrows, d_model, z, gamma, beta, eps, y);
+    if (!rc && z_out) memcpy(z_out, z, sizeof(double) * (size_t)(nrows * d_model));
+  }
+  free(h); free(z);
   return rc;
 }
 

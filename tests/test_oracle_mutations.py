@@ -41,6 +41,11 @@ MUTATIONS = {
                              "for (int x = 0; x < c->d_k; ++x) dkj[x] += ds * qi[x];"),
     "bwd dV from the wrong weight": ("for (int x = 0; x < c->d_v; ++x) dvj[x] += P[j] * doi[x];",
                                      "for (int x = 0; x < c->d_v; ++x) dvj[x] += ds * doi[x];"),
+    "PE sine and cosine swapped": ("(c & 1) ? cos(angle) : sin(angle);", "(c & 1) ? sin(angle) : cos(angle);"),
+    "PE exponent i instead of 2i": ("int i2 = c - (c & 1);", "int i2 = (c - (c & 1)) / 2;"),
+    "LayerNorm unbiased variance": ("var /= d;", "var /= (d - 1);"),
+    "LayerNorm eps outside the root": ("double rstd = 1.0 / sqrt(var + eps);", "double rstd = 1.0 / (sqrt(var) + eps);"),
+    "sublayer without the residual": ("for (int64_t t = 0; t < nz; ++t) z[t] += h[t];", "for (int64_t t = 0; t < 0; ++t) z[t] += h[t];"),
     "projection weight transposed": ("for (int n = 0; n < g->N; ++n) c[n] += ak * wk[n];",
                                      "for (int n = 0; n < g->N; ++n) c[n] += ak * g->w[(int64_t)n * g->K + kk];"),
 }

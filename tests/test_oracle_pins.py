@@ -527,3 +527,122 @@ def test_bwd_special_cases():
     assert np.allclose(dv[0, :, 0], dout[0].sum(axis=1), rtol=0, atol=1e-13)
     z = oracle.sdpa_bwd(q, k, v, np.zeros_like(dout))
     assert all(np.all(g == 0) for g in z)
+
+
+# ---- positional encoding, LayerNorm and the attention sublayer --------------
+def test_pe_closed_forms():
+    """Position 0: every sine column is 0 and every cosine column 1.  The
+    first pair has frequency 1 (10000^0), so its columns are sin(pos) and
+    cos(pos) (the formula of paper section 3.5 on the vlmlib.cn summary and
+    rockcohen.cc section 5.4)."""
+    pe = oracle.positional_encoding(50, 16)
+    assert np.all(pe[0, 0::2] == 0.0) and np.all(pe[0, 1::2] == 1.0)
+    pos = np.arange(50)
+    assert np.allclose(pe[:, 0], np.sin(pos), rtol=0, atol=1e-15)
+    assert np.allclose(pe[:, 1], np.cos(pos), rtol=0, atol=1e-15)
+    assert np.allclose(pe[:, 0::2] ** 2 + pe[:, 1::2] ** 2, 1.0, rtol=0, atol=1e-15)
+
+
+def test_pe_wavelengths_geometric_from_2pi_to_10000_2pi():
+    """rockcohen.cc section 5.4: the wavelengths form a geometric progression
+    from 2*pi towards 10000*2*pi.  The angle of pair i at position 1 is its
+    frequency; consecutive ratios are equal, the first frequency is 1 and the
+    d/2-th power of the ratio is 1/10000."""
+    d = 64
+    pe = oracle.positional_encoding(2, d)
+    w = np.arctan2(pe[1, 0::2], pe[1, 1::2])          # angle of each pair at pos = 1
+    assert abs(w[0] - 1.0) < 1e-15
+    ratio = w[1:] / w[:-1]
+    assert np.allclose(ratio, ratio[0], rtol=1e-12, atol=0)
+    assert abs(ratio[0] ** (d // 2) - 1e-4) < 1e-15
+
+
+def test_pe_offset_is_a_linear_map():
+    """For a fixed offset k, PE(pos + k) is a linear function of PE(pos) (the
+    reason the paper gives for sinusoids, section 3.5: vlmlib.cn summary;
+    rockcohen.cc section 5.4).  The map is built from PE(k) alone: each
+    (sin, cos) pair rotates by its angle at position k."""
+    d, n = 10, 60
+    pe = oracle.positional_encoding(n, d)
+    for k in (1, 7, 23):
+        s_k, c_k = pe[k, 0::2], pe[k, 1::2]
+        for pos in (0, 3, 17, n - 1 - k):
+            s, c = pe[pos, 0::2], pe[pos, 1::2]
+            pred = np.empty(d)
+            pred[0::2] = s * c_k + c * s_k                # sin(a + b)
+            pred[1::2] = c * c_k - s * s_k                # cos(a + b)
+            assert np.allclose(pe[pos + k], pred, rtol=0, atol=1e-12)
+
+
+def test_layernorm_scale_and_shift_invariance():
+    """rockcohen.cc section 5.5 (reproduction P6): LN(c z) = LN(z) for c = 1e3
+    and 1e-3, and LN(z + 1) = LN(z): LayerNorm removes the mean and the scale
+    of a row (eps = 0 here)."""
+    z = rnd(700, (5, 12))
+    g, b = np.ones(12), np.zeros(12)
+    base = oracle.layernorm(z, g, b, 0.0)
+    for c in (1e3, 1e-3):
+        assert np.abs(oracle.layernorm(c * z, g, b, 0.0) - base).max() < 1e-12
+    assert np.abs(oracle.layernorm(z + 1.0, g, b, 0.0) - base).max() < 1e-12
+    assert np.abs(oracle.layernorm(3.0 * z - 7.0, g, b, 0.0) - base).max() < 1e-12
+
+
+def test_layernorm_moments_and_affine():
+    """With gain 1 and bias 0 each row has mean 0 and mean square 1 (the
+    population variance: dividing by d, not d - 1); the gain and bias then
+    act per column; eps sits inside the square root: the row [-1, 1] has
+    variance 1, so it maps to gamma*(+-1)/sqrt(1 + eps) + beta; a constant row
+    maps to beta."""
+    z = rnd(701, (4, 9))
+    y = oracle.layernorm(z, np.ones(9), np.zeros(9), 0.0)
+    assert np.abs(y.mean(axis=1)).max() < 1e-14
+    assert np.abs((y ** 2).mean(axis=1) - 1.0).max() < 1e-13
+    g, b = rnd(702, (9,)), rnd(703, (9,))
+    assert np.abs(oracle.layernorm(z, g, b, 0.0) - (y * g + b)).max() < 1e-13
+    eps = 0.25
+    y2 = oracle.layernorm(np.array([[-1.0, 1.0]]), np.array([2.0, 3.0]), np.array([0.5, -0.5]), eps)
+    assert np.allclose(y2, [[-2.0 / np.sqrt(1.25) + 0.5, 3.0 / np.sqrt(1.25) - 0.5]], rtol=0, atol=1e-15)
+    y3 = oracle.layernorm(np.full((1, 5), 4.2), np.ones(5), np.arange(5.0), 1e-5)
+    assert np.array_equal(y3, np.arange(5.0)[None, :])
+
+
+def _block_inputs(seed, B=2, n=7, dm=8, heads=2, d=4):
+    x = rnd(seed, (B, n, dm))
+    ws = [rnd(seed + 1 + t, shape) * 0.3 for t, shape in
+          enumerate([(dm, heads * d), (dm, heads * d), (dm, heads * d), (heads * d, dm)])]
+    g, b = 1.0 + 0.1 * rnd(seed + 5, (dm,)), 0.1 * rnd(seed + 6, (dm,))
+    return x, ws, g, b
+
+
+def test_block_is_layernorm_of_residual_plus_mha():
+    """The sublayer is LayerNorm(h + MultiHead(h)) with h = x + PE (paper
+    section 3.1 post-LN, vlmlib.cn summary; section 3.5 for the PE), checked
+    against the separately pinned parts; with W^O = 0 the attention adds
+    nothing and y = LN(x + PE); with gain 0, y = beta exactly."""
+    x, (wq, wk, wv, wo), g, b = _block_inputs(710)
+    h = x + oracle.positional_encoding(7, 8)[None]
+    y, z = oracle.mha_block(x, wq, wk, wv, wo, g, b, heads=2, add_pe=True, eps=1e-5, causal=True)
+    m = oracle.mha(h, h, wq, wk, wv, wo, heads=2, causal=True)
+    assert np.abs(z - (h + m)).max() < 1e-13
+    assert np.abs(y - oracle.layernorm(h + m, g, b, 1e-5)).max() < 1e-13
+    y0, _ = oracle.mha_block(x, wq, wk, wv, np.zeros_like(wo), g, b, heads=2, add_pe=True, eps=1e-5)
+    assert np.abs(y0 - oracle.layernorm(h, g, b, 1e-5)).max() < 1e-13
+    yb, _ = oracle.mha_block(x, wq, wk, wv, wo, np.zeros(8), b, heads=2, add_pe=True)
+    assert np.array_equal(yb, np.broadcast_to(b, yb.shape))
+
+
+def test_block_cross_and_rows():
+    """Cross-attention sublayer: z = x_q + MultiHead(x_q, x_kv, x_kv), no PE;
+    the row-selected form equals the full one."""
+    x, (wq, wk, wv, wo), g, b = _block_inputs(720)
+    xkv = rnd(727, (2, 5, 8))
+    y, z = oracle.mha_block(x, wq, wk, wv, wo, g, b, heads=2, x_kv=xkv, seqlens_kv=[5, 2])
+    m = oracle.mha(x, xkv, wq, wk, wv, wo, heads=2, seqlens_kv=[5, 2])
+    assert np.abs(z - (x + m)).max() < 1e-13
+    rows = [0, 6, 9, 13]
+    yr, zr = oracle.mha_block_rows(x, wq, wk, wv, wo, g, b, heads=2, rows=rows, x_kv=xkv,
+                                   seqlens_kv=[5, 2])
+    assert np.array_equal(yr, y.reshape(-1, 8)[rows]) and np.array_equal(zr, z.reshape(-1, 8)[rows])
+    ys, _ = oracle.mha_block(x, wq, wk, wv, wo, g, b, heads=2, add_pe=True, causal=True)
+    ysr, _ = oracle.mha_block_rows(x, wq, wk, wv, wo, g, b, heads=2, rows=rows, add_pe=True, causal=True)
+    assert np.array_equal(ysr, ys.reshape(-1, 8)[rows])
