@@ -290,3 +290,21 @@ def backward_workload(**overrides) -> tuple[SDPAInputs, np.ndarray, np.ndarray]:
                     p["n"], p["n"], 64, 64, 0.125, True, cfg_id=8)
     g, g_st = make_dout(inp, 8)
     return inp, g, g_st
+
+
+def sublayer_workload(**overrides):
+    """The attention sublayer of the big model at the block's shape: token
+    embeddings X [4, 4096, 1024] ~ N(0,1) (the positional encoding is added by
+    the sublayer itself), Xavier W^Q, W^K, W^V, W^O [1024, 1024], LayerNorm
+    gain 1 + 0.1 N(0,1) and bias 0.1 N(0,1), h = 16, causal; all bf16.  Seeds
+    1000*9 + t (t = 0 X, 4..7 the weights, 8 and 9 gain and bias).
+    `overrides` may shrink any size.  Returns (x, [w_q, w_k, w_v, w_o], gamma,
+    beta, heads) as exact fp64 values."""
+    p = dict(B=4, n=4096, d_model=1024, heads=16)
+    p.update(overrides)
+    B, n, dm, h = p["B"], p["n"], p["d_model"], p["heads"]
+    x = to_dtype(normal(_seed(9, 0), (B, n, dm)), "bf16")
+    ws = [to_dtype(xavier_uniform(_seed(9, 4 + t), dm, dm), "bf16") for t in range(4)]
+    gamma = to_dtype(1.0 + 0.1 * normal(_seed(9, 8), (dm,)), "bf16")
+    beta = to_dtype(0.1 * normal(_seed(9, 9), (dm,)), "bf16")
+    return x, ws, gamma, beta, h

@@ -2,7 +2,7 @@
 """Benchmark of the attention forward hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload decoder|encoder|cross|block|decode|window|backward]
+                    [--workload decoder|encoder|cross|block|decode|window|backward|sublayer]
 
 A step is one pass of the hot path over one batch of synthetic input that is
 already resident in HBM:
@@ -17,6 +17,8 @@ already resident in HBM:
                      radius 256
   backward           gradients dQ, dK, dV of causal attention at the block's
                      shape, [4, 16, 4096, 64] (the forward's o and lse given)
+  sublayer           the attention sublayer LayerNorm(h + MultiHead(h)),
+                     h = X + PE, X [4, 4096, 1024], h = 16, causal
 Inputs rotate over enough copies to exceed the 256 MB Infinity Cache (cold
 cache), the K timed steps are captured once in a HIP graph and replayed, and
 HIP events on the launch stream bracket the replay.  Rank 0 prints one JSON
@@ -43,7 +45,7 @@ METRIC = "attention fwd TFLOP/s (bf16) + % of MFMA peak, h=8 d_k=64 n=256 causal
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 CACHE_BYTES = 256 << 20       # Infinity Cache
-WORKLOAD_CFG = {"encoder": 2, "decoder": 3, "cross": 4, "block": 5, "decode": 6, "window": 7, "backward": 8}
+WORKLOAD_CFG = {"encoder": 2, "decoder": 3, "cross": 4, "block": 5, "decode": 6, "window": 7, "backward": 8, "sublayer": 9}
 
 
 def legal_pairs(n_q, n_kv, causal, lq=None, lkv=None, batch=1):
@@ -65,6 +67,7 @@ KERNEL_FILES = {
     "decoder": ["sdpa_fwd_bf16.hip"], "encoder": ["sdpa_fwd_bf16.hip"], "cross": ["sdpa_fwd_bf16.hip"],
     "window": ["sdpa_fwd_bf16.hip"], "block": ["sdpa_fwd_bf16.hip", "gemm_bf16.hip"],
     "decode": ["sdpa_decode_bf16.hip"], "backward": ["sdpa_bwd_bf16.hip"],
+    "sublayer": ["sdpa_fwd_bf16.hip", "gemm_bf16.hip", "mha_block_bf16.hip"],
 }
 
 
@@ -472,10 +475,84 @@ def bench_backward(K, W, args):
     return result, inp, flops
 
 
+def bench_sublayer(K, W, args):
+    """The attention sublayer at the big model's shape: y = LayerNorm(h +
+    MultiHead(h)), h = X + PE, X [4, 4096, 1024], h = 16, causal, one
+    attn_mha_block_fwd call per step (encoding pass, QKV GEMM, SDPA, W^O GEMM
+    with the residual and LayerNorm in its epilogue).  The same block without
+    the encoding and LayerNorm (attn_mha_fwd) is timed alongside."""
+    import torch
+    import attn_inputs as gen
+    import head_attention_sdpa_amd as attn
+
+    L = attn.lib()
+    dev = torch.device("cuda:0")
+    x64, ws64, g64, b64, h = gen.sublayer_workload()
+    B, n, dm = x64.shape
+    hd = h * 64
+    x = to_dev(gen.bf16_bits(x64), "bf16", dev)
+    ws = [to_dev(gen.bf16_bits(w), "bf16", dev) for w in ws64]
+    gam, bet = to_dev(gen.bf16_bits(g64), "bf16", dev), to_dev(gen.bf16_bits(b64), "bf16", dev)
+    nbytes = attn.mha_block_workspace_bytes(B, n, n, dm, h, True)
+    work = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    y = torch.empty((B, n, dm), dtype=torch.bfloat16, device=dev)
+    scale = 0.125
+
+    def launch(s):
+        rc = L.attn_mha_block_fwd(attn.ATTN_BF16, B, n, n, dm, h, 64, 64, x.data_ptr(), x.data_ptr(), 1,
+                                  ws[0].data_ptr(), ws[1].data_ptr(), ws[2].data_ptr(), ws[3].data_ptr(),
+                                  gam.data_ptr(), bet.data_ptr(), 1e-5, y.data_ptr(), scale,
+                                  attn.ATTN_MASK_CAUSAL, None, None, work.data_ptr(), nbytes,
+                                  torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"attn_mha_block_fwd failed: {attn.status_str(rc)}")
+
+    ms, _ = time_graph(launch, K, W, torch)
+    y2 = torch.empty_like(y)
+    nb2 = attn.mha_workspace_bytes(B, n, n, dm, h)
+
+    def launch_plain(s):
+        rc = L.attn_mha_fwd(attn.ATTN_BF16, B, n, n, dm, h, 64, 64, x.data_ptr(), x.data_ptr(),
+                            ws[0].data_ptr(), ws[1].data_ptr(), ws[2].data_ptr(), ws[3].data_ptr(),
+                            y2.data_ptr(), scale, attn.ATTN_MASK_CAUSAL, None, None,
+                            work.data_ptr(), nb2, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"attn_mha_fwd failed: {attn.status_str(rc)}")
+
+    ms_plain, _ = time_graph(launch_plain, max(10, K), W, torch)
+    pairs = legal_pairs(n, n, True, batch=1) * B * h
+    flops = pairs * 256 + 2 * B * n * 3 * hd * dm + 2 * B * n * hd * dm
+    tflops = flops / (ms * 1e-3) / 1e12
+    result = {
+        "metric": "attention sublayer TFLOP/s (bf16) + % of MFMA peak, X [4,4096,1024] h=16 causal, PE + LayerNorm",
+        "value": tflops, "ms_per_step": ms, "pct_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "config": {"workload": "sublayer_bf16_4x4096x1024_h16_causal_pe_ln", "batch": B, "n": n,
+                   "d_model": dm, "heads": h, "d_k": 64, "causal": True, "add_pe": True, "ln_eps": 1e-5,
+                   "cache": "hot (inputs 40 MB, written intermediates reused)",
+                   "timing": "HIP graph of the timed steps, HIP events on the launch stream",
+                   "flops_per_step": flops, "flops_counted": "projections 2*M*N*K, attention 4*d per legal pair",
+                   "block_without_pe_ln_ms": ms_plain},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / PEAK_BF16_TFLOPS, "traffic": read_traffic("sublayer"),
+                     "kernel": "attn_mha_block_fwd (pe_add_bf16 + gemm_bf16_dma_kernel + sdpa_fwd_bf16_d64 + "
+                               "gemm_bf16_ln_kernel), timed as one call",
+                     "algorithmic_flops_per_launch": flops},
+    }
+    return result, (x64, ws64, g64, b64, h), flops
+
+
 def cpu_baseline(cfg_id, inp, flops_full):
     """The oracle as it stands, on the host cores, on a bounded sample."""
     import oracle
     threads = oracle.default_threads()
+    if cfg_id == 9:
+        x, ws, g, b, h = inp
+        t0 = time.perf_counter()
+        oracle.mha_block(x[:1], *ws, g, b, heads=h, add_pe=True, eps=1e-5, scale=0.125, causal=True,
+                         nthreads=threads)
+        dt = time.perf_counter() - t0
+        return {"value": flops_full / x.shape[0] / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+                "kind": "oracle", "sample": "batch element 0 of 4 (all 4096 rows), one run", "seconds": dt}
     if cfg_id == 8:
         t0 = time.perf_counter()
         oracle.sdpa_bwd(inp.q, inp.k, inp.v, inp.dout, scale=inp.scale, causal=True, nthreads=threads)
@@ -568,6 +645,8 @@ def main():
         res, inp, flops = bench_window(K, W, args)
     elif cfg_id == 8:
         res, inp, flops = bench_backward(K, W, args)
+    elif cfg_id == 9:
+        res, inp, flops = bench_sublayer(K, W, args)
     else:
         res, inp, flops = bench_sdpa(cfg_id, K, W, args)
     out = {"metric": res.get("metric", METRIC), "value": res["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": K,

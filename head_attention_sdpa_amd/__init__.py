@@ -29,7 +29,8 @@ STATUS = {0: "ATTN_OK", -1: "ATTN_E_INVALID", -2: "ATTN_E_UNSUPPORTED", -3: "ATT
 
 # every entry point that include/attn_sdpa.h declares
 EXPORTS = ("attn_sdpa_fwd", "attn_sdpa_window_fwd", "attn_mha_workspace_bytes", "attn_mha_fwd", "attn_decode_workspace_bytes",
-           "attn_decode_fwd", "attn_linear_fwd", "attn_sdpa_bwd_workspace_bytes", "attn_sdpa_bwd",
+           "attn_decode_fwd", "attn_linear_fwd", "attn_mha_block_workspace_bytes", "attn_mha_block_fwd",
+           "attn_sdpa_bwd_workspace_bytes", "attn_sdpa_bwd",
            "attn_status_str", "attn_abi_version")
 
 
@@ -73,6 +74,11 @@ def lib() -> ctypes.CDLL:
         L.attn_decode_fwd.restype = i
         L.attn_linear_fwd.argtypes = [i, i, i, i, vp, ctypes.c_int64, vp, vp, ctypes.c_int64, vp]
         L.attn_linear_fwd.restype = i
+        L.attn_mha_block_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i]
+        L.attn_mha_block_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_mha_block_fwd.argtypes = [i, i, i, i, i, i, i, i, vp, vp, i, vp, vp, vp, vp, vp, vp,
+                                         ctypes.c_float, vp, ctypes.c_float, i, vp, vp, vp, ctypes.c_size_t, vp]
+        L.attn_mha_block_fwd.restype = i
         L.attn_sdpa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
         L.attn_sdpa_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.attn_sdpa_bwd.argtypes = [i, i, i, i, i, i, i, vp, sp, vp, sp, vp, sp, vp, sp, vp, sp, vp,
@@ -203,6 +209,48 @@ def mha(x_q, x_kv, w_q, w_k, w_v, w_o, heads, scale=None, causal=False, seqlens_
                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                             _stream(stream))
     _check("attn_mha_fwd", rc)
+    return out
+
+
+def mha_block_workspace_bytes(batch, n_q, n_kv, d_model, heads, add_pe, d_k=64, d_v=64,
+                              dtype=ATTN_BF16) -> int:
+    return int(lib().attn_mha_block_workspace_bytes(dtype, batch, n_q, n_kv, d_model, heads, d_k, d_v,
+                                                    int(bool(add_pe))))
+
+
+def mha_block(x_q, w_q, w_k, w_v, w_o, ln_gamma, ln_beta, heads, x_kv=None, add_pe=False, ln_eps=1e-5,
+              scale=None, causal=False, seqlens_q=None, seqlens_kv=None, out=None, workspace=None,
+              stream=None):
+    """The attention sublayer on the GPU (bf16, d_k = d_v = 64, d_model in
+    {256, 512, 768, 1024}): y = LayerNorm(h + MultiHead(h, kv, kv)) with
+    h = x_q (+ positional encoding if add_pe) and kv = h (x_kv None:
+    self-attention) or x_kv.  Returns y [B, n_q, d_model]."""
+    torch = _torch()
+    B, n_q, d_model = x_q.shape
+    xkv = x_q if x_kv is None else x_kv
+    n_kv = xkv.shape[1]
+    for t in (x_q, xkv, w_q, w_k, w_v, w_o, ln_gamma, ln_beta):
+        if not t.is_contiguous() or t.device != x_q.device or t.dtype != x_q.dtype:
+            raise ValueError("mha_block inputs must be contiguous and share device and dtype")
+    dt = _dtype_code(x_q)
+    nbytes = mha_block_workspace_bytes(B, n_q, n_kv, d_model, heads, add_pe, w_q.shape[1] // heads,
+                                       w_v.shape[1] // heads, dt)
+    if nbytes == 0:
+        raise AttnError("attn_mha_block_workspace_bytes", -2, "unsupported sizes")
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x_q.device)
+    if out is None:
+        out = torch.empty((B, n_q, d_model), dtype=x_q.dtype, device=x_q.device)
+    rc = lib().attn_mha_block_fwd(dt, B, n_q, n_kv, d_model, heads, w_q.shape[1] // heads,
+                                  w_v.shape[1] // heads, x_q.data_ptr(), xkv.data_ptr(),
+                                  int(bool(add_pe)), w_q.data_ptr(), w_k.data_ptr(), w_v.data_ptr(),
+                                  w_o.data_ptr(), ln_gamma.data_ptr(), ln_beta.data_ptr(), float(ln_eps),
+                                  out.data_ptr(), 0.0 if scale is None else float(scale),
+                                  ATTN_MASK_CAUSAL if causal else ATTN_MASK_NONE,
+                                  _lens_ptr(seqlens_q, B, x_q.device), _lens_ptr(seqlens_kv, B, x_q.device),
+                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  _stream(stream))
+    _check("attn_mha_block_fwd", rc)
     return out
 
 

@@ -221,9 +221,84 @@ size_t bwd_workspace(int batch, int heads, int n_q) {
   return round256((size_t)batch * heads * n_q * 2 * sizeof(float));
 }
 
+// Steps 1-2 of the multi-head block: the Q/K/V projections of x_q and x_kv
+// (one GEMM over three weight panels for self-attention) and the attention of
+// every head, written as the concatenation [B*n_q, H*64] at the workspace's
+// o_off.  Shapes and pointers are validated by the caller.
+int mha_project_attend(int batch, int n_q, int n_kv, int d_model, int heads, const uint16_t* xq,
+                       const uint16_t* xkv, bool self_attn, const void* w_q, const void* w_k,
+                       const void* w_v, float scale, attn_mask mask, const int32_t* seqlens_q,
+                       const int32_t* seqlens_kv, char* ws, const MhaLayout& L, hipStream_t stream) {
+  uint16_t* qbuf = reinterpret_cast<uint16_t*>(ws + L.q_off);
+  uint16_t* kvbuf = reinterpret_cast<uint16_t*>(ws + L.kv_off);
+  uint16_t* obuf = reinterpret_cast<uint16_t*>(ws + L.o_off);
+  const int hd = heads * 64;
+  attn_strides st[4];
+  const uint16_t *qp, *kp, *vp;
+  int rc;
+  if (self_attn) {
+    // self-attention: one GEMM over the three weight panels,
+    // [Q | K | V] = X [W^Q | W^K | W^V] -> [B*n, 3*H*64] at the start of the
+    // workspace (it fits before the concatenation region)
+    GemmBf16Params g = {};
+    g.a = xq;
+    g.b[0] = static_cast<const uint16_t*>(w_q);
+    g.b[1] = static_cast<const uint16_t*>(w_k);
+    g.b[2] = static_cast<const uint16_t*>(w_v);
+    g.c = qbuf;
+    g.lda = d_model; g.ldc = 3 * hd; g.M = batch * n_q; g.N = 3 * hd; g.K = d_model; g.n_panel = hd;
+    rc = hip_status(attn::launch_gemm_bf16(g, stream));
+    st[0] = attn_strides{(int64_t)n_q * 3 * hd, 64, 3 * hd};
+    st[1] = st[2] = st[0];
+    qp = qbuf;
+    kp = qbuf + hd;
+    vp = qbuf + 2 * hd;
+  } else {
+    // cross-attention: Q = X_q W^Q -> [B*n_q, H*64];
+    // [K | V] = X_kv [W^K | W^V] -> [B*n_kv, 2*H*64]
+    GemmBf16Params gq = {};
+    gq.a = xq;
+    gq.b[0] = static_cast<const uint16_t*>(w_q);
+    gq.c = qbuf;
+    gq.lda = d_model; gq.ldc = hd; gq.M = batch * n_q; gq.N = hd; gq.K = d_model; gq.n_panel = hd;
+    GemmBf16Params gkv = {};
+    gkv.a = xkv;
+    gkv.b[0] = static_cast<const uint16_t*>(w_k);
+    gkv.b[1] = static_cast<const uint16_t*>(w_v);
+    gkv.c = kvbuf;
+    gkv.lda = d_model; gkv.ldc = 2 * hd; gkv.M = batch * n_kv; gkv.N = 2 * hd; gkv.K = d_model;
+    gkv.n_panel = hd;
+    rc = hip_status(attn::launch_gemm_bf16(gq, stream));
+    if (rc == ATTN_OK) rc = hip_status(attn::launch_gemm_bf16(gkv, stream));
+    st[0] = attn_strides{(int64_t)n_q * hd, 64, hd};
+    st[1] = attn_strides{(int64_t)n_kv * 2 * hd, 64, 2 * hd};
+    st[2] = st[1];
+    qp = qbuf;
+    kp = kvbuf;
+    vp = kvbuf + hd;
+  }
+  if (rc != ATTN_OK) return rc;
+  // attention per head, reading the projections through strides and writing
+  // the concatenation [B, n_q, H, 64] directly
+  st[3] = attn_strides{(int64_t)n_q * hd, 64, hd};
+  return launch_sdpa(ATTN_BF16, batch, heads, n_q, n_kv, 64, 64, qp, kp, vp, obuf, st, scale, mask, -1,
+                     seqlens_q, seqlens_kv, nullptr, stream);
+}
+
+// The sublayer's extra workspace: h = x + PE [B*n_q, d_model] after the MHA
+// regions (only when the encoding is added).
+size_t block_h_off(const MhaLayout& L) { return L.total_bytes; }
+size_t block_total(const MhaLayout& L, int batch, int n_q, int d_model, bool add_pe) {
+  return L.total_bytes + (add_pe ? round256((size_t)batch * n_q * d_model * 2) : 0);
+}
+bool block_dmodel_ok(int d_model) {
+  return d_model == 256 || d_model == 512 || d_model == 768 || d_model == 1024;
+}
+
 }  // namespace
 
 extern "C" {
+
 
 int attn_abi_version(void) { return ATTN_ABI_VERSION; }
 
@@ -293,71 +368,88 @@ int attn_mha_fwd(attn_dtype dt, int batch, int n_q, int n_kv, int d_model, int h
 
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   char* ws = static_cast<char*>(workspace);
-  uint16_t* qbuf = reinterpret_cast<uint16_t*>(ws + L.q_off);
-  uint16_t* kvbuf = reinterpret_cast<uint16_t*>(ws + L.kv_off);
-  uint16_t* obuf = reinterpret_cast<uint16_t*>(ws + L.o_off);
-  const int hd = heads * 64;
-
-  attn_strides st[4];
-  const uint16_t *qp, *kp, *vp;
-  int rc;
-  if (x_kv == x_q && n_kv == n_q) {
-    // 1. self-attention: one GEMM over the three weight panels,
-    //    [Q | K | V] = X [W^Q | W^K | W^V] -> [B*n, 3*H*64] at the start of the
-    //    workspace (it fits before the concatenation region)
-    GemmBf16Params g = {};
-    g.a = static_cast<const uint16_t*>(x_q);
-    g.b[0] = static_cast<const uint16_t*>(w_q);
-    g.b[1] = static_cast<const uint16_t*>(w_k);
-    g.b[2] = static_cast<const uint16_t*>(w_v);
-    g.c = qbuf;
-    g.lda = d_model; g.ldc = 3 * hd; g.M = batch * n_q; g.N = 3 * hd; g.K = d_model; g.n_panel = hd;
-    rc = hip_status(attn::launch_gemm_bf16(g, stream));
-    st[0] = attn_strides{(int64_t)n_q * 3 * hd, 64, 3 * hd};
-    st[1] = st[2] = st[0];
-    qp = qbuf;
-    kp = qbuf + hd;
-    vp = qbuf + 2 * hd;
-  } else {
-    // 1. cross-attention: Q = X_q W^Q -> [B*n_q, H*64];
-    //    [K | V] = X_kv [W^K | W^V] -> [B*n_kv, 2*H*64]
-    GemmBf16Params gq = {};
-    gq.a = static_cast<const uint16_t*>(x_q);
-    gq.b[0] = static_cast<const uint16_t*>(w_q);
-    gq.c = qbuf;
-    gq.lda = d_model; gq.ldc = hd; gq.M = batch * n_q; gq.N = hd; gq.K = d_model; gq.n_panel = hd;
-    GemmBf16Params gkv = {};
-    gkv.a = static_cast<const uint16_t*>(x_kv);
-    gkv.b[0] = static_cast<const uint16_t*>(w_k);
-    gkv.b[1] = static_cast<const uint16_t*>(w_v);
-    gkv.c = kvbuf;
-    gkv.lda = d_model; gkv.ldc = 2 * hd; gkv.M = batch * n_kv; gkv.N = 2 * hd; gkv.K = d_model;
-    gkv.n_panel = hd;
-    rc = hip_status(attn::launch_gemm_bf16(gq, stream));
-    if (rc == ATTN_OK) rc = hip_status(attn::launch_gemm_bf16(gkv, stream));
-    st[0] = attn_strides{(int64_t)n_q * hd, 64, hd};
-    st[1] = attn_strides{(int64_t)n_kv * 2 * hd, 64, 2 * hd};
-    st[2] = st[1];
-    qp = qbuf;
-    kp = kvbuf;
-    vp = kvbuf + hd;
-  }
-  if (rc != ATTN_OK) return rc;
-
-  // 2. attention per head, reading the projections through strides and
-  //    writing the concatenation [B, n_q, H, 64] directly
-  st[3] = attn_strides{(int64_t)n_q * hd, 64, hd};
-  rc = launch_sdpa(ATTN_BF16, batch, heads, n_q, n_kv, 64, 64, qp, kp, vp, obuf, st, scale, mask, -1,
-                   seqlens_q, seqlens_kv, nullptr, stream);
+  const bool self_attn = x_kv == x_q && n_kv == n_q;
+  int rc = mha_project_attend(batch, n_q, n_kv, d_model, heads, static_cast<const uint16_t*>(x_q),
+                              static_cast<const uint16_t*>(x_kv), self_attn, w_q, w_k, w_v, scale, mask,
+                              seqlens_q, seqlens_kv, ws, L, stream);
   if (rc != ATTN_OK) return rc;
 
   // 3. output projection: Y = Ocat W^O -> [B*n_q, d_model]
+  const int hd = heads * 64;
   GemmBf16Params go = {};
-  go.a = obuf;
+  go.a = reinterpret_cast<const uint16_t*>(ws + L.o_off);
   go.b[0] = static_cast<const uint16_t*>(w_o);
   go.c = static_cast<uint16_t*>(y);
   go.lda = hd; go.ldc = d_model; go.M = batch * n_q; go.N = d_model; go.K = hd; go.n_panel = d_model;
   return hip_status(attn::launch_gemm_bf16(go, stream));
+}
+
+size_t attn_mha_block_workspace_bytes(attn_dtype dt, int batch, int n_q, int n_kv, int d_model,
+                                      int heads, int d_k, int d_v, int add_pe) {
+  int err;
+  if (!mha_sizes_ok(dt, batch, n_q, n_kv, d_model, heads, d_k, d_v, &err) || !block_dmodel_ok(d_model))
+    return 0;
+  return block_total(mha_layout(batch, n_q, n_kv, heads), batch, n_q, d_model, add_pe != 0);
+}
+
+int attn_mha_block_fwd(attn_dtype dt, int batch, int n_q, int n_kv, int d_model, int heads, int d_k,
+                       int d_v, const void* x_q, const void* x_kv, int add_pe, const void* w_q,
+                       const void* w_k, const void* w_v, const void* w_o, const void* ln_gamma,
+                       const void* ln_beta, float ln_eps, void* y, float scale, attn_mask mask,
+                       const int32_t* seqlens_q, const int32_t* seqlens_kv, void* workspace,
+                       size_t workspace_bytes, attn_stream_t stream_) {
+  int err = ATTN_OK;
+  if (!mha_sizes_ok(dt, batch, n_q, n_kv, d_model, heads, d_k, d_v, &err)) return err;
+  if (!block_dmodel_ok(d_model)) return ATTN_E_UNSUPPORTED;
+  if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL) return ATTN_E_INVALID;
+  if (!x_q || !x_kv || !w_q || !w_k || !w_v || !w_o || !ln_gamma || !ln_beta || !y) return ATTN_E_INVALID;
+  const bool self_attn = x_kv == x_q;
+  if (self_attn && n_kv != n_q) return ATTN_E_INVALID;
+  if (add_pe != 0 && add_pe != 1) return ATTN_E_INVALID;
+  if (add_pe && !self_attn) return ATTN_E_INVALID;     // the encoding belongs to the sublayer's own input
+  if (!(isfinite(ln_eps) && ln_eps > 0.f)) return ATTN_E_INVALID;
+  if (scale == 0.f) scale = 1.f / sqrtf((float)d_k);
+  if (!(isfinite(scale) && scale > 0.f)) return ATTN_E_INVALID;
+  const void* ptrs[] = {x_q, x_kv, w_q, w_k, w_v, w_o, ln_gamma, ln_beta, y};
+  for (const void* p : ptrs)
+    if (!aligned(p, 16)) return ATTN_E_ALIGN;
+  const MhaLayout L = mha_layout(batch, n_q, n_kv, heads);
+  if (!workspace || workspace_bytes < block_total(L, batch, n_q, d_model, add_pe != 0))
+    return ATTN_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return ATTN_E_ALIGN;
+  if (n_q == 0) return ATTN_OK;   // no output rows: nothing to do
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  char* ws = static_cast<char*>(workspace);
+  const uint16_t* h = static_cast<const uint16_t*>(x_q);
+  int rc = ATTN_OK;
+  if (add_pe) {
+    // 0. h = x + PE, the sublayer's input and its residual
+    uint16_t* hb = reinterpret_cast<uint16_t*>(ws + block_h_off(L));
+    attn::PeAddParams pp = {};
+    pp.x = static_cast<const uint16_t*>(x_q);
+    pp.h = hb;
+    pp.ldx = d_model; pp.ldh = d_model;
+    pp.batch = batch; pp.n = n_q; pp.d_model = d_model;
+    rc = hip_status(attn::launch_pe_add_bf16(pp, stream));
+    h = hb;
+  }
+  if (rc != ATTN_OK) return rc;
+  rc = mha_project_attend(batch, n_q, n_kv, d_model, heads, h, self_attn ? h : static_cast<const uint16_t*>(x_kv),
+                          self_attn, w_q, w_k, w_v, scale, mask, seqlens_q, seqlens_kv, ws, L, stream);
+  if (rc != ATTN_OK) return rc;
+  // 3. y = LayerNorm(h + Ocat W^O) in the output projection's epilogue
+  attn::GemmLnParams gl = {};
+  gl.a = reinterpret_cast<const uint16_t*>(ws + L.o_off);
+  gl.w = static_cast<const uint16_t*>(w_o);
+  gl.res = h;
+  gl.gamma = static_cast<const uint16_t*>(ln_gamma);
+  gl.beta = static_cast<const uint16_t*>(ln_beta);
+  gl.y = static_cast<uint16_t*>(y);
+  gl.lda = heads * 64; gl.ldr = d_model; gl.ldy = d_model;
+  gl.M = batch * n_q; gl.N = d_model; gl.K = heads * 64;
+  gl.eps = ln_eps;
+  return hip_status(attn::launch_gemm_bf16_ln(gl, stream));
 }
 
 int attn_linear_fwd(attn_dtype dt, int m, int k, int n, const void* x, int64_t ldx, const void* w,

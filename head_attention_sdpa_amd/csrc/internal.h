@@ -110,6 +110,30 @@ struct GemmBf16Params {
   int n_panel;                  // columns per B panel (N = panels * n_panel)
 };
 
+// h = RNE(x + PE) for x [batch, n, d_model] bf16 (row strides ldx, ldh
+// elements), PE the sinusoidal positional encoding of position i.
+struct PeAddParams {
+  const uint16_t* x;
+  uint16_t* h;
+  int64_t ldx, ldh;
+  int batch, n, d_model;        // d_model a multiple of 8
+};
+
+// y = LayerNorm(res + a . w) over the N = d_model columns of each row: a
+// [M, K] (row stride lda), w [K, N] row-major contiguous, res and y [M, N]
+// (row strides ldr, ldy), gamma and beta [N]; all bf16, fp32 arithmetic.
+struct GemmLnParams {
+  const uint16_t* a;
+  const uint16_t* w;
+  const uint16_t* res;
+  const uint16_t* gamma;
+  const uint16_t* beta;
+  uint16_t* y;
+  int64_t lda, ldr, ldy;
+  int M, N, K;                  // N in {256, 512, 768, 1024}, K a multiple of 16
+  float eps;
+};
+
 // Launchers: return hipSuccess or the launch error.  Shapes are validated by
 // the caller (abi.cpp) before these are reached.
 hipError_t launch_sdpa_bf16(const SdpaBf16Params& p, hipStream_t stream);
@@ -117,6 +141,8 @@ hipError_t launch_sdpa_f32(const SdpaF32Params& p, hipStream_t stream);
 hipError_t launch_sdpa_decode_bf16(const SdpaDecodeParams& p, hipStream_t stream);
 hipError_t launch_sdpa_bwd_bf16(const SdpaBwdParams& p, hipStream_t stream);
 hipError_t launch_gemm_bf16(const GemmBf16Params& p, hipStream_t stream);
+hipError_t launch_pe_add_bf16(const PeAddParams& p, hipStream_t stream);
+hipError_t launch_gemm_bf16_ln(const GemmLnParams& p, hipStream_t stream);
 bool gemm_bf16_main_supported(const GemmBf16Params& p);   // shapes the fast kernel takes
 
 // Queries per workgroup of the bf16 SDPA kernel chosen for these sizes.

@@ -26,6 +26,13 @@
  *   attn_linear_fwd one projection of that block on its own, Y = X.W (the
  *                  products X W_i^Q, X W_i^K, X W_i^V and Concat(...) W^O of
  *                  section 3.2.2; rockcohen.cc 5.2).
+ *   attn_mha_block_fwd  the attention sublayer around the block, post-LN:
+ *                  y = LayerNorm(h + MultiHead(h, kv, kv)), h = x (+ the
+ *                  sinusoidal positional encoding), with the residual add and
+ *                  LayerNorm fused into the output projection (paper sections
+ *                  3.1 and 3.5 on the vlmlib.cn summary; rockcohen.cc sections
+ *                  5.4 and 5.5; the LN formula on the ai-master transformer_lab
+ *                  page).
  *   attn_sdpa_bwd  gradients of Eq. 1 with respect to Q, K and V for a given
  *                  gradient of O (the model is trained end to end: the
  *                  vlmlib.cn summary's training-objective paragraph;
@@ -64,7 +71,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 5
+#define ATTN_ABI_VERSION 6
 
 typedef void* attn_stream_t; /* hipStream_t */
 
@@ -228,6 +235,44 @@ int attn_decode_fwd(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int 
  */
 int attn_linear_fwd(attn_dtype dt, int m, int k, int n, const void* x, int64_t ldx, const void* w,
                     void* y, int64_t ldy, attn_stream_t stream);
+
+/*
+ * attn_mha_block_workspace_bytes -- workspace attn_mha_block_fwd needs: that
+ * of attn_mha_fwd plus, with add_pe, h [batch, n_q, d_model] bf16; 0 when the
+ * sizes are invalid or unsupported.
+ */
+size_t attn_mha_block_workspace_bytes(attn_dtype dt, int batch, int n_q, int n_kv, int d_model,
+                                      int heads, int d_k, int d_v, int add_pe);
+
+/*
+ * attn_mha_block_fwd -- the attention sublayer of the encoder and decoder:
+ *
+ *   h = x_q + PE       if add_pe (PE[i][2j] = sin(i / 10000^(2j/d_model)),
+ *                      PE[i][2j+1] = cos(...), position i from 0; h is rounded
+ *                      to bf16 once); else h = x_q
+ *   z = h + MultiHead(h, kv, kv)     kv = h when x_kv == x_q (self-attention),
+ *                                    else x_kv (cross-attention)
+ *   y = ln_gamma * (z - mean(z)) / sqrt(var(z) + ln_eps) + ln_beta
+ *                      per position, mean and population variance over the
+ *                      d_model features, z kept in fp32 (never stored)
+ *
+ *   x_q [batch, n_q, d_model], x_kv [batch, n_kv, d_model], y [batch, n_q,
+ *   d_model]; w_* as for attn_mha_fwd; ln_gamma, ln_beta [d_model]; all bf16,
+ *   contiguous, 16-byte aligned.  dt = ATTN_BF16, d_k = d_v = 64,
+ *   d_model in {256, 512, 768, 1024} (otherwise ATTN_E_UNSUPPORTED).
+ *   add_pe is 0 or 1 and needs x_kv == x_q (and then n_kv == n_q); ln_eps
+ *   finite and > 0; scale, mask and the lengths as for attn_mha_fwd (rows
+ *   i >= L_q get the attention output 0, so their y is LayerNorm(h)).
+ *   workspace: attn_mha_block_workspace_bytes(...) bytes, 256-byte aligned.
+ * y must not overlap any input or the workspace.  Returns ATTN_OK or a
+ * negative attn_status; nothing is enqueued on error.
+ */
+int attn_mha_block_fwd(attn_dtype dt, int batch, int n_q, int n_kv, int d_model, int heads, int d_k,
+                       int d_v, const void* x_q, const void* x_kv, int add_pe, const void* w_q,
+                       const void* w_k, const void* w_v, const void* w_o, const void* ln_gamma,
+                       const void* ln_beta, float ln_eps, void* y, float scale, attn_mask mask,
+                       const int32_t* seqlens_q, const int32_t* seqlens_kv, void* workspace,
+                       size_t workspace_bytes, attn_stream_t stream);
 
 /*
  * attn_sdpa_bwd_workspace_bytes -- workspace attn_sdpa_bwd needs for these

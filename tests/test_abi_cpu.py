@@ -228,3 +228,44 @@ def test_bwd_workspace_bytes():
     assert L.attn_sdpa_bwd_workspace_bytes(1, 1, 1, 0, 5, 64, 64) == 0
     assert L.attn_sdpa_bwd_workspace_bytes(0, 1, 1, 3, 5, 64, 64) == 0      # f32 unsupported
     assert L.attn_sdpa_bwd_workspace_bytes(1, 1, 1, 3, 5, 32, 32) == 0
+
+
+def block_call(dt=1, B=2, nq=64, nkv=64, dm=256, H=4, dk=64, dv=64, xq=FAKE, xkv=FAKE, pe=1, g=FAKE,
+               b=FAKE, eps=1e-5, y=FAKE, mask=1, ws=FAKE, wsb=1 << 30, scale=0.0):
+    return attn.lib().attn_mha_block_fwd(dt, B, nq, nkv, dm, H, dk, dv, xq, xkv, pe, FAKE, FAKE, FAKE, FAKE,
+                                         g, b, eps, y, scale, mask, None, None, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), -1),
+    (dict(B=0), -1),
+    (dict(mask=3), -1),
+    (dict(g=None), -1),
+    (dict(y=None), -1),
+    (dict(pe=2), -1),
+    (dict(xkv=FAKE + 4096), -1),             # encoding on a cross-attention sublayer
+    (dict(nkv=32), -1),                      # self-attention with n_kv != n_q
+    (dict(eps=0.0), -1),
+    (dict(eps=float("inf")), -1),
+    (dict(scale=-1.0), -1),
+    (dict(dt=0), -2),
+    (dict(dm=320), -2),                      # d_model outside {256, 512, 768, 1024}
+    (dict(dm=2048, H=32), -2),
+    (dict(dk=32, dv=32), -2),
+    (dict(g=MISALIGNED), -3),
+    (dict(ws=FAKE + 64), -3),
+    (dict(ws=None), -4),
+    (dict(wsb=1024), -4),
+    (dict(nq=0, nkv=0), 0),                  # no output rows: nothing to do
+])
+def test_mha_block_validation(kw, code):
+    assert block_call(**kw) == code
+
+
+def test_mha_block_workspace_bytes():
+    L = attn.lib()
+    # the MHA regions (Q | K | V and the concatenation, bf16) plus h with the encoding
+    base = L.attn_mha_workspace_bytes(1, 4, 4096, 4096, 1024, 16, 64, 64)
+    assert L.attn_mha_block_workspace_bytes(1, 4, 4096, 4096, 1024, 16, 64, 64, 0) == base
+    assert L.attn_mha_block_workspace_bytes(1, 4, 4096, 4096, 1024, 16, 64, 64, 1) == base + 4 * 4096 * 1024 * 2
+    assert L.attn_mha_block_workspace_bytes(1, 4, 4096, 4096, 320, 5, 64, 64, 0) == 0
