@@ -416,8 +416,9 @@ def bench_decode(K, W, args):
 
 def bench_backward(K, W, args):
     """Gradients of causal attention at the block's shape, [4, 16, 4096, 64]
-    bf16: one attn_sdpa_bwd call per step (D and lse preprocessing, the dK/dV
-    kernel, the dQ kernel), given q, k, v, the forward's o and lse, and dO.
+    bf16: one attn_sdpa_bwd call per step (the dQ kernel, which also forms D
+    and the log2 lse, then the dK/dV kernel), given q, k, v, the forward's o
+    and lse, and dO.
     Work is counted algorithmically, 10*d FLOPs per legal pair (the products
     Q.K^T, dO.V^T, P^T.dO, dS^T.Q and dS.K); the kernels recompute Q.K^T and
     dO.V^T once more in the dQ pass (14*d executed)."""
@@ -467,7 +468,7 @@ def bench_backward(K, W, args):
                    "algorithmic_bytes_per_step": algo_bytes},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / PEAK_BF16_TFLOPS, "traffic": read_traffic("backward"),
-                     "kernel": "attn_sdpa_bwd (sdpa_bwd_pre + sdpa_bwd_dkdv + sdpa_bwd_dq), timed as one call",
+                     "kernel": "attn_sdpa_bwd (sdpa_bwd_dq, then sdpa_bwd_dkdv), timed as one call",
                      "algorithmic_flops_per_launch": flops,
                      "hbm_frac": algo_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
     }

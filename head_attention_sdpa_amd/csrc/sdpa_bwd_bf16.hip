@@ -7,11 +7,14 @@
 //   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),   dQ = scale dS K,
 //   dK = scale dS^T Q.
 // P is recomputed from the scores and the forward's log-sum-exp, exp(s - lse),
-// so nothing of size n_q x n_kv is stored.  Three kernels:
+// so nothing of size n_q x n_kv is stored.  Two kernels, in this order:
 //
-//   sdpa_bwd_pre       per query row: D (fp32) and lse in log2 units (+inf for
-//                      padded rows and rows without keys, so their weights are
-//                      exactly 0), into the workspace.
+//   sdpa_bwd_dq        workgroup = (b, h, 128 queries), the forward's
+//                      decomposition: S^T = K Q^T and dP^T = V dO^T with one
+//                      query per lane column, dQ^T += K^T dS^T.  It first
+//                      forms each row's D (fp32) and lse in log2 units (+inf
+//                      for padded rows and rows without keys, so their weights
+//                      are exactly 0) and leaves them in the workspace.
 //   sdpa_bwd_dkdv      workgroup = (b, h, 128 keys), wave w owns 32 keys and
 //                      keeps their K and V fragments in registers; query tiles
 //                      of 64 (Q, dO and the per-row terms) stream through an
@@ -22,9 +25,6 @@
 //                      the queries in the order the C layout gives them; the
 //                      dO^T and Q^T operands are read transposed in the same
 //                      order).
-//   sdpa_bwd_dq        workgroup = (b, h, 128 queries), the forward's
-//                      decomposition: S^T = K Q^T and dP^T = V dO^T with one
-//                      query per lane column, dQ^T += K^T dS^T.
 //
 // Every product is v_mfma_f32_32x32x16_bf16 (fp32 accumulation); P and dS are
 // rounded to bf16 for the products, and dQ, dK, dV once to bf16 at the store.
@@ -88,35 +88,6 @@ __device__ __forceinline__ bf16x8 pack8(const float* x) {
     r[t + 1] = h[1];
   }
   return r;
-}
-
-// ---------------------------------------------------------------------------
-// 8 lanes per query row: D = dO . O (fp32) and the log2-unit lse.
-__global__ __launch_bounds__(256) void sdpa_bwd_pre(const SdpaBwdParams p) {
-  const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
-  const int sub = threadIdx.x & 7;
-  const int64_t rows = (int64_t)p.batch * p.heads * p.n_q;
-  if (row >= rows) return;                      // whole 8-lane groups leave together
-  const int i = (int)(row % p.n_q);
-  const int64_t bh = row / p.n_q;
-  const int b = (int)(bh / p.heads), h = (int)(bh - (int64_t)b * p.heads);
-  int Lq = p.n_q;
-  if (p.seqlens_q) Lq = min(max(p.seqlens_q[b], 0), p.n_q);
-  const __bf16* orow = reinterpret_cast<const __bf16*>(p.o) + b * p.os_b + h * p.os_h + (int64_t)i * p.os_n;
-  const __bf16* drow = reinterpret_cast<const __bf16*>(p.dout) + b * p.dos_b + h * p.dos_h + (int64_t)i * p.dos_n;
-  const bf16x8 ov = *reinterpret_cast<const bf16x8*>(orow + 8 * sub);
-  const bf16x8 dv = *reinterpret_cast<const bf16x8*>(drow + 8 * sub);
-  float dot = 0.f;
-#pragma unroll
-  for (int t = 0; t < 8; ++t) dot = fmaf((float)ov[t], (float)dv[t], dot);
-  dot += __shfl_xor(dot, 1, 8);
-  dot += __shfl_xor(dot, 2, 8);
-  dot += __shfl_xor(dot, 4, 8);
-  if (sub == 0) {
-    const float lse = p.lse[row];
-    const bool valid = i < Lq && lse > -INFINITY;
-    *reinterpret_cast<f32x2*>(p.ld + 2 * row) = valid ? f32x2{lse * LOG2E, dot} : f32x2{INFINITY, 0.f};
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -328,7 +299,10 @@ void sdpa_bwd_dq(const SdpaBwdParams p) {
   const int nblk = (kv_end + BT - 1) / BT;
 
   // Q and dO fragments of this lane's query (B operands: lane = query, k = d),
-  // its lse2 and D; padded rows read zeros and lse2 = +inf (weights 0)
+  // its lse2 = lse*log2(e) and D = dO . O (lanes l and l^32 hold the two
+  // halves of d); padded rows and rows with no key read zeros and get
+  // lse2 = +inf (weights 0).  The (lse2, D) pairs also go to the workspace,
+  // where the dK/dV kernel, launched next, reads them.
   bf16x8 qf[4], df[4];
   float lse2 = INFINITY, dd = 0.f;
   {
@@ -336,18 +310,26 @@ void sdpa_bwd_dq(const SdpaBwdParams p) {
     const int ii = qvalid ? qi : 0;
     const __bf16* qrow = reinterpret_cast<const __bf16*>(p.q) + b * p.qs_b + h * p.qs_h + (int64_t)ii * p.qs_n;
     const __bf16* drow = reinterpret_cast<const __bf16*>(p.dout) + b * p.dos_b + h * p.dos_h + (int64_t)ii * p.dos_n;
+    const __bf16* orow = reinterpret_cast<const __bf16*>(p.o) + b * p.os_b + h * p.os_h + (int64_t)ii * p.os_n;
+    float dot = 0.f;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(qrow + 16 * d + 8 * g);
       const bf16x8 c = *reinterpret_cast<const bf16x8*>(drow + 16 * d + 8 * g);
+      const bf16x8 o = *reinterpret_cast<const bf16x8*>(orow + 16 * d + 8 * g);
       qf[d] = qvalid ? a : bf16x8{};
       df[d] = qvalid ? c : bf16x8{};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) dot = fmaf((float)c[t], (float)o[t], dot);
     }
-    const f32x2 l = *reinterpret_cast<const f32x2*>(p.ld + 2 * ((int64_t)bh * p.n_q + ii));
-    if (qvalid) {
-      lse2 = l[0];
-      dd = l[1];
+    dot = sum_with_partner(dot);
+    const float lse = p.lse[(int64_t)bh * p.n_q + ii];
+    if (qvalid && lse > -INFINITY) {
+      lse2 = lse * LOG2E;
+      dd = dot;
     }
+    if (g == 0 && qi < p.n_q)
+      *reinterpret_cast<f32x2*>(p.ld + 2 * ((int64_t)bh * p.n_q + qi)) = f32x2{lse2, dd};
 #pragma unroll
     for (int d = 0; d < 4; ++d) asm volatile("" ::"v"(qf[d]), "v"(df[d]));
     asm volatile("" ::"v"(lse2), "v"(dd));
@@ -452,21 +434,16 @@ void sdpa_bwd_dq(const SdpaBwdParams p) {
 hipError_t launch_sdpa_bwd_bf16(const SdpaBwdParams& p, hipStream_t stream) {
   const int64_t bh = (int64_t)p.batch * p.heads;
   if (bh == 0) return hipSuccess;
+  // dQ first: it also writes the (lse2, D) pairs the dK/dV kernel reads
   if (p.n_q > 0) {
-    const int64_t rows = bh * p.n_q;
-    hipLaunchKernelGGL(sdpa_bwd_pre, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, stream, p);
+    const int64_t grid = (int64_t)((p.n_q + 127) / 128) * bh;
+    hipLaunchKernelGGL(sdpa_bwd_dq<2>, dim3((unsigned)grid), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (p.n_kv > 0) {
     const int64_t grid = (int64_t)((p.n_kv + 127) / 128) * bh;
     hipLaunchKernelGGL(sdpa_bwd_dkdv<2>, dim3((unsigned)grid), dim3(256), 0, stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (p.n_q > 0) {
-    const int64_t grid = (int64_t)((p.n_q + 127) / 128) * bh;
-    hipLaunchKernelGGL(sdpa_bwd_dq<2>, dim3((unsigned)grid), dim3(256), 0, stream, p);
   }
   return hipGetLastError();
 }
