@@ -242,7 +242,7 @@ def mha_block(x_q, w_q, w_k, w_v, w_o, ln_gamma, ln_beta, heads, x_kv=None, add_
     if out is None:
         out = torch.empty((B, n_q, d_model), dtype=x_q.dtype, device=x_q.device)
     rc = lib().attn_mha_block_fwd(dt, B, n_q, n_kv, d_model, heads, w_q.shape[1] // heads,
-                                  w_v.shape[1] // heads, x_q.data_ptr(), xkv.data_ptr(),
+                                  w_v.shape[1] // heads, x_q.data_ptr(), xkv.data_ptr() or None,
                                   int(bool(add_pe)), w_q.data_ptr(), w_k.data_ptr(), w_v.data_ptr(),
                                   w_o.data_ptr(), ln_gamma.data_ptr(), ln_beta.data_ptr(), float(ln_eps),
                                   out.data_ptr(), 0.0 if scale is None else float(scale),

@@ -356,7 +356,7 @@ int attn_mha_fwd(attn_dtype dt, int batch, int n_q, int n_kv, int d_model, int h
   int err = ATTN_OK;
   if (!mha_sizes_ok(dt, batch, n_q, n_kv, d_model, heads, d_k, d_v, &err)) return err;
   if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL) return ATTN_E_INVALID;
-  if (!x_q || !x_kv || !w_q || !w_k || !w_v || !w_o || !y) return ATTN_E_INVALID;
+  if (!x_q || (!x_kv && n_kv > 0) || !w_q || !w_k || !w_v || !w_o || !y) return ATTN_E_INVALID;
   if (scale == 0.f) scale = 1.f / sqrtf((float)d_k);
   if (!(isfinite(scale) && scale > 0.f)) return ATTN_E_INVALID;
   const void* ptrs[] = {x_q, x_kv, w_q, w_k, w_v, w_o, y};
@@ -402,7 +402,8 @@ int attn_mha_block_fwd(attn_dtype dt, int batch, int n_q, int n_kv, int d_model,
   if (!mha_sizes_ok(dt, batch, n_q, n_kv, d_model, heads, d_k, d_v, &err)) return err;
   if (!block_dmodel_ok(d_model)) return ATTN_E_UNSUPPORTED;
   if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL) return ATTN_E_INVALID;
-  if (!x_q || !x_kv || !w_q || !w_k || !w_v || !w_o || !ln_gamma || !ln_beta || !y) return ATTN_E_INVALID;
+  if (!x_q || (!x_kv && n_kv > 0) || !w_q || !w_k || !w_v || !w_o || !ln_gamma || !ln_beta || !y)
+    return ATTN_E_INVALID;
   const bool self_attn = x_kv == x_q;
   if (self_attn && n_kv != n_q) return ATTN_E_INVALID;
   if (add_pe != 0 && add_pe != 1) return ATTN_E_INVALID;

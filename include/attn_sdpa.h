@@ -152,7 +152,8 @@ size_t attn_mha_workspace_bytes(attn_dtype dt, int batch, int n_q, int n_kv, int
  * formula of section 3.2.2).
  *
  *   x_q   [batch, n_q,  d_model] bf16 (queries; the decoder side)
- *   x_kv  [batch, n_kv, d_model] bf16 (keys/values; may equal x_q)
+ *   x_kv  [batch, n_kv, d_model] bf16 (keys/values; may equal x_q; may be
+ *         NULL when n_kv = 0, which gives zero attention output)
  *   w_q, w_k  [d_model, heads*d_k] row-major, Y = X.W (head h owns columns
  *             [h*d_k, (h+1)*d_k))
  *   w_v       [d_model, heads*d_v]
@@ -256,9 +257,9 @@ size_t attn_mha_block_workspace_bytes(attn_dtype dt, int batch, int n_q, int n_k
  *                      per position, mean and population variance over the
  *                      d_model features, z kept in fp32 (never stored)
  *
- *   x_q [batch, n_q, d_model], x_kv [batch, n_kv, d_model], y [batch, n_q,
- *   d_model]; w_* as for attn_mha_fwd; ln_gamma, ln_beta [d_model]; all bf16,
- *   contiguous, 16-byte aligned.  dt = ATTN_BF16, d_k = d_v = 64,
+ *   x_q [batch, n_q, d_model], x_kv [batch, n_kv, d_model] (may be NULL when
+ *   n_kv = 0), y [batch, n_q, d_model]; w_* as for attn_mha_fwd; ln_gamma,
+ *   ln_beta [d_model]; all bf16, contiguous, 16-byte aligned.  dt = ATTN_BF16, d_k = d_v = 64,
  *   d_model in {256, 512, 768, 1024} (otherwise ATTN_E_UNSUPPORTED).
  *   add_pe is 0 or 1 and needs x_kv == x_q (and then n_kv == n_q); ln_eps
  *   finite and > 0; scale, mask and the lengths as for attn_mha_fwd (rows

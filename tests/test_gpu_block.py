@@ -87,6 +87,10 @@ CASES = [
          cross=True, lkv=[97, 40]),
     dict(name="self_no_pe_d1024", B=1, n_q=130, n_kv=130, dm=1024, heads=16, causal=True, add_pe=False),
     dict(name="one_row_tile_tail", B=3, n_q=21, n_kv=21, dm=256, heads=2, causal=False, add_pe=True),
+    dict(name="cross_empty_memory", B=2, n_q=70, n_kv=0, dm=256, heads=4, causal=False, add_pe=False,
+         cross=True),
+    dict(name="cross_causal_nq_gt_nkv", B=1, n_q=200, n_kv=90, dm=512, heads=8, causal=True, add_pe=False,
+         cross=True),
 ]
 
 

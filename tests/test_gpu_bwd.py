@@ -66,7 +66,7 @@ def bounds(q, k, v, g, o_gpu, lse, scale, causal, Lq, Lkv, ref):
 
 
 def run_case(name, B, H, n_q, n_kv, causal, lq=None, lkv=None, seed=0, check_heads=None,
-             strided=False, zero_dout=False):
+             strided=False, zero_dout=False, strided_grads=False):
     import torch
     attn = attn_mod()
     inp = gen.make_sdpa(name, "bf16", B, H, n_q, n_kv, 64, 64, 0.125, causal,
@@ -91,8 +91,18 @@ def run_case(name, B, H, n_q, n_kv, causal, lq=None, lkv=None, seed=0, check_hea
         k, v = packed(k, 1, n_kv), packed(v, 2, n_kv)
     lqg, lkg = lens_gpu(inp.seqlens_q), lens_gpu(inp.seqlens_kv)
     o, lse = attn.sdpa(q, k, v, scale=0.125, causal=causal, seqlens_q=lqg, seqlens_kv=lkg, return_lse=True)
+    grads = {}
+    if strided_grads:
+        # dq, dk, dv written into views of packed [B, n, H, 2*64] buffers
+        gq = torch.full((B, n_q, H, 128), float("nan"), dtype=torch.bfloat16, device=q.device)
+        gkv = torch.full((B, n_kv, H, 256), float("nan"), dtype=torch.bfloat16, device=q.device)
+        grads = dict(dq=gq[..., 64:].permute(0, 2, 1, 3), dk=gkv[..., :64].permute(0, 2, 1, 3),
+                     dv=gkv[..., 128:192].permute(0, 2, 1, 3))
     dq, dk, dv = attn.sdpa_bwd(q, k, v, o, lse, do, scale=0.125, causal=causal, seqlens_q=lqg,
-                               seqlens_kv=lkg)
+                               seqlens_kv=lkg, **grads)
+    if strided_grads:   # the rest of the packed buffers is untouched
+        assert torch.isnan(gq[..., :64]).all() and torch.isnan(gkv[..., 64:128]).all()
+        assert torch.isnan(gkv[..., 192:]).all()
     torch.cuda.synchronize()
     og, lg = to_f64(o), lse.double().cpu().numpy()
     got = [to_f64(t) for t in (dq, dk, dv)]
@@ -135,6 +145,9 @@ CASES = [
     dict(name="zero_length_sequence", B=2, H=2, n_q=150, n_kv=150, causal=True, lq=[0, 150], lkv=[150, 0]),
     dict(name="strided_packed", B=2, H=3, n_q=190, n_kv=190, causal=True, lkv=[190, 77], strided=True),
     dict(name="multi_tile", B=1, H=2, n_q=700, n_kv=700, causal=False),
+    dict(name="query_lengths_only", B=2, H=2, n_q=180, n_kv=180, causal=False, lq=[180, 61]),
+    dict(name="strided_gradients", B=2, H=2, n_q=150, n_kv=150, causal=True, lkv=[150, 99],
+         strided_grads=True),
 ]
 
 
