@@ -120,7 +120,7 @@ void sdpa_bwd_dkdv(const SdpaBwdParams p) {
   if (nqt < 0) nqt = 0;
 
   const __bf16* Qb = reinterpret_cast<const __bf16*>(p.q) + b * p.qs_b + h * p.qs_h;
-  const __bf16* Ob = reinterpret_cast<const __bf16*>(p.dout) + b * p.dos_b + h * p.dos_h;
+  const __bf16* DOb = reinterpret_cast<const __bf16*>(p.dout) + b * p.dos_b + h * p.dos_h;
   const float* LDb = p.ld + (int64_t)bh * p.n_q * 2;
   const uint32_t q_bytes = Lq > 0 ? (uint32_t)((int64_t)(Lq - 1) * p.qs_n * 2 + 128) : 0u;
   const uint32_t o_bytes = Lq > 0 ? (uint32_t)((int64_t)(Lq - 1) * p.dos_n * 2 + 128) : 0u;
@@ -162,7 +162,7 @@ void sdpa_bwd_dkdv(const SdpaBwdParams p) {
     const int q0 = (qt_begin + j) * BT;
     const int64_t q_adv = (int64_t)q0 * p.qs_n, o_adv = (int64_t)q0 * p.dos_n;
     const i32x4 rq = make_rsrc(Qb + q_adv, (uint32_t)max<int64_t>(0, (int64_t)q_bytes - 2 * q_adv));
-    const i32x4 ro = make_rsrc(Ob + o_adv, (uint32_t)max<int64_t>(0, (int64_t)o_bytes - 2 * o_adv));
+    const i32x4 ro = make_rsrc(DOb + o_adv, (uint32_t)max<int64_t>(0, (int64_t)o_bytes - 2 * o_adv));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int u = wave * 4 + i;
