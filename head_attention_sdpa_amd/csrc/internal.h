@@ -63,7 +63,7 @@ struct SdpaBwdParams {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* ld;                    // workspace [batch*heads*n_q][2]: lse*log2(e) (+inf: no weight), D = dO.O;
+  float* ld;                    // workspace: lse*log2(e) [batch*heads*n_q] (+inf: no weight), then -D = -dO.O [batch*heads*n_q];
                                 // written by the dQ kernel, read by the dK/dV kernel
   const int32_t* seqlens_q;
   const int32_t* seqlens_kv;

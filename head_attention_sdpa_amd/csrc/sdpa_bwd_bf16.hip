@@ -96,10 +96,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void sdpa_bwd_dkdv(const SdpaBwdParams p) {
   constexpr int BK = 128;                  // keys per workgroup (4 waves x 32)
   constexpr int STAGE_E = 2 * TILE_E;      // Q tile, dO tile
-  constexpr int IPT = 5;                   // DMA instructions per wave per stage: 4 of Q/dO, 1 of (lse2, D)
+  constexpr int IPT = 4;                   // Q/dO DMA instructions per wave per stage (+1 for waves 0, 1)
   static_assert(NS >= 2 && NS <= 4, "bad configuration");
   __shared__ __attribute__((aligned(1024))) __bf16 smem[NS * STAGE_E];
-  __shared__ __attribute__((aligned(1024))) float lds_ld[NS][4][256];   // per stage, per wave: 128 (lse2, D)
+  __shared__ __attribute__((aligned(1024))) float lds_l2[NS][256];   // per stage: lse2 of queries q0..q0+255
+  __shared__ __attribute__((aligned(1024))) float lds_nd[NS][256];   // per stage: -D of the same queries
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -121,10 +122,12 @@ void sdpa_bwd_dkdv(const SdpaBwdParams p) {
 
   const __bf16* Qb = reinterpret_cast<const __bf16*>(p.q) + b * p.qs_b + h * p.qs_h;
   const __bf16* DOb = reinterpret_cast<const __bf16*>(p.dout) + b * p.dos_b + h * p.dos_h;
-  const float* LDb = p.ld + (int64_t)bh * p.n_q * 2;
+  const int64_t rows_all = (int64_t)bhn * p.n_q;
+  const float* L2b = p.ld + (int64_t)bh * p.n_q;              // lse2 plane
+  const float* NDb = p.ld + rows_all + (int64_t)bh * p.n_q;   // -D plane
   const uint32_t q_bytes = Lq > 0 ? (uint32_t)((int64_t)(Lq - 1) * p.qs_n * 2 + 128) : 0u;
   const uint32_t o_bytes = Lq > 0 ? (uint32_t)((int64_t)(Lq - 1) * p.dos_n * 2 + 128) : 0u;
-  const uint32_t ld_bytes = (uint32_t)p.n_q * 8;
+  const uint32_t ld_bytes = (uint32_t)p.n_q * 4;
 
   // K and V fragments of the wave's 32 keys (B operands: lane = key, k = d);
   // keys past the length read as zeros.
@@ -170,8 +173,12 @@ void sdpa_bwd_dkdv(const SdpaBwdParams p) {
       const __bf16* dst = smem + (j % NS) * STAGE_E + (is_o ? TILE_E : 0) + (u & 7) * 512;
       dma16(dma_off[i], is_o ? ro : rq, lds_addr(dst));
     }
-    const i32x4 rl = make_rsrc(LDb + 2 * (int64_t)q0, (uint32_t)max<int64_t>(0, (int64_t)ld_bytes - 8 * (int64_t)q0));
-    dma16((uint32_t)(lane * 16), rl, lds_addr(&lds_ld[j % NS][wave][0]));
+    // the per-row terms of the tile's queries: wave 0 copies lse2, wave 1 -D
+    if (wave < 2) {
+      const i32x4 rl = make_rsrc((wave == 0 ? L2b : NDb) + q0,
+                                 (uint32_t)max<int64_t>(0, (int64_t)ld_bytes - 4 * (int64_t)q0));
+      dma16((uint32_t)(lane * 16), rl, lds_addr(wave == 0 ? &lds_l2[j % NS][0] : &lds_nd[j % NS][0]));
+    }
   };
 
 #pragma unroll
@@ -182,14 +189,16 @@ void sdpa_bwd_dkdv(const SdpaBwdParams p) {
   const float c2 = p.scale_log2;
 
   for (int t = 0; t < nqt; ++t) {
-    wait_vmcnt_le<IPT>(min(NS - 2, nqt - 1 - t) * IPT);
+    if (wave < 2) wait_vmcnt_le<IPT + 1>(min(NS - 2, nqt - 1 - t) * (IPT + 1));
+    else wait_vmcnt_le<IPT>(min(NS - 2, nqt - 1 - t) * IPT);
     barrier_lds();   // stage t visible; every wave is done with stage t-1
     if (t + NS - 1 < nqt) issue_stage(t + NS - 1);
     const int q0 = (qt_begin + t) * BT;
     if (p.causal && q0 + BT - 1 < kw0) continue;   // wave-uniform: every query before the wave's keys
     const __bf16* Qs = smem + (t % NS) * STAGE_E;
     const __bf16* Ds = Qs + TILE_E;
-    const float* lt = &lds_ld[t % NS][wave][0];
+    const float* lt2 = &lds_l2[t % NS][0];
+    const float* ltd = &lds_nd[t % NS][0];
     // Only the causal mask needs applying: rows past L_q have lse2 = +inf
     // (weight 0), rows past n_q and keys past L_kv read as zeros, so their dS
     // and dO are 0 and they add nothing to the legal keys' columns; the
@@ -198,14 +207,22 @@ void sdpa_bwd_dkdv(const SdpaBwdParams p) {
     const int qlo = kj - q0 - 4 * g;   // legal: query offset (in the tile, less 4*g) >= qlo
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      // S = Q K^T and dP = dO V^T for queries q0 + 32*qb + row(r): lane = key
-      f32x16 s = {}, dp = {};
+      // S = Q K^T and dP - D = dO V^T - D for queries q0 + 32*qb + row(r):
+      // lane = key; register r is query 32*qb + 8*(r/4) + 4*g + r%4 of the
+      // tile, so the -D of four consecutive queries starts each register
+      // group of the dP accumulator
+      f32x16 s = {}, dp;
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const f32x4 nd = *reinterpret_cast<const f32x4*>(ltd + 32 * qb + 8 * rg + 4 * g);
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) dp[4 * rg + t4] = nd[t4];
+      }
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         s = mfma32(rows_frag(Qs, 32 * qb + i32, d, g), kf[d], s);
         dp = mfma32(rows_frag(Ds, 32 * qb + i32, d, g), vf[d], dp);
       }
-      // register r is query 32*qb + 8*(r/4) + 4*g + r%4 of the tile
       if (diag) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -215,17 +232,13 @@ void sdpa_bwd_dkdv(const SdpaBwdParams p) {
       float pv[16], dsv[16];
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const int ql = 32 * qb + 8 * rg + 4 * g;
-        const f32x4 a = *reinterpret_cast<const f32x4*>(lt + 2 * ql);       // (lse2, D) of queries ql, ql+1
-        const f32x4 bq = *reinterpret_cast<const f32x4*>(lt + 2 * ql + 4);  // ql+2, ql+3
-        const float l2[4] = {a[0], a[2], bq[0], bq[2]};
-        const float dd[4] = {a[1], a[3], bq[1], bq[3]};
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(lt2 + 32 * qb + 8 * rg + 4 * g);
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) {
           const int r = 4 * rg + t4;
           const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2[t4]));
           pv[r] = pr;
-          dsv[r] = pr * (dp[r] - dd[t4]);
+          dsv[r] = pr * dp[r];
         }
       }
       // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries of this block
@@ -301,7 +314,7 @@ void sdpa_bwd_dq(const SdpaBwdParams p) {
   // Q and dO fragments of this lane's query (B operands: lane = query, k = d),
   // its lse2 = lse*log2(e) and D = dO . O (lanes l and l^32 hold the two
   // halves of d); padded rows and rows with no key read zeros and get
-  // lse2 = +inf (weights 0).  The (lse2, D) pairs also go to the workspace,
+  // lse2 = +inf (weights 0).  lse2 and -D also go to the workspace planes,
   // where the dK/dV kernel, launched next, reads them.
   bf16x8 qf[4], df[4];
   float lse2 = INFINITY, dd = 0.f;
@@ -328,8 +341,11 @@ void sdpa_bwd_dq(const SdpaBwdParams p) {
       lse2 = lse * LOG2E;
       dd = dot;
     }
-    if (g == 0 && qi < p.n_q)
-      *reinterpret_cast<f32x2*>(p.ld + 2 * ((int64_t)bh * p.n_q + qi)) = f32x2{lse2, dd};
+    if (g == 0 && qi < p.n_q) {
+      const int64_t row = (int64_t)bh * p.n_q + qi;
+      p.ld[row] = lse2;                                    // lse2 plane
+      p.ld[(int64_t)bhn * p.n_q + row] = -dd;              // -D plane
+    }
 #pragma unroll
     for (int d = 0; d < 4; ++d) asm volatile("" ::"v"(qf[d]), "v"(df[d]));
     asm volatile("" ::"v"(lse2), "v"(dd));
