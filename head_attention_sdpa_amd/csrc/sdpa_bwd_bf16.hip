@@ -450,7 +450,7 @@ void sdpa_bwd_dq(const SdpaBwdParams p) {
 hipError_t launch_sdpa_bwd_bf16(const SdpaBwdParams& p, hipStream_t stream) {
   const int64_t bh = (int64_t)p.batch * p.heads;
   if (bh == 0) return hipSuccess;
-  // dQ first: it also writes the (lse2, D) pairs the dK/dV kernel reads
+  // dQ first: it also writes the lse2 and -D planes the dK/dV kernel reads
   if (p.n_q > 0) {
     const int64_t grid = (int64_t)((p.n_q + 127) / 128) * bh;
     hipLaunchKernelGGL(sdpa_bwd_dq<2>, dim3((unsigned)grid), dim3(256), 0, stream, p);
