@@ -371,13 +371,10 @@ hipError_t launch_gemm_bf16(const GemmBf16Params& p, hipStream_t stream) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
   if (gemm_bf16_main_supported(p)) {
     const int64_t tiles = (int64_t)((p.M + M2 - 1) / M2) * (p.N / N2);
-    hipLaunchKernelGGL((gemm_bf16_dma_kernel<kStages>), dim3((unsigned)tiles), dim3(64 * NWAVES), 0, stream,
-                       p);
-    return hipGetLastError();
+    return launch_kernel(gemm_bf16_dma_kernel<kStages>, dim3((unsigned)tiles), dim3(64 * NWAVES), stream, p);
   }
   const int64_t tiles = (int64_t)((p.M + BM - 1) / BM) * ((p.N + BNt - 1) / BNt);
-  hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)tiles), dim3(NT), 0, stream, p);
-  return hipGetLastError();
+  return launch_kernel(gemm_bf16_kernel, dim3((unsigned)tiles), dim3(NT), stream, p);
 }
 
 }  // namespace attn

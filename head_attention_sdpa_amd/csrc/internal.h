@@ -135,6 +135,16 @@ struct GemmLnParams {
   float eps;
 };
 
+// Enqueues kernel<<<grid, block, 0, stream>>>(p) and returns the status of
+// this launch alone.  (hipGetLastError after a launch would also return an
+// error left behind by any earlier call on the same host thread, made by
+// another library, and blame it on this launch.)
+template <typename P>
+inline hipError_t launch_kernel(void (*kernel)(P), dim3 grid, dim3 block, hipStream_t stream, const P& p) {
+  void* args[] = {const_cast<P*>(&p)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, stream);
+}
+
 // Launchers: return hipSuccess or the launch error.  Shapes are validated by
 // the caller (abi.cpp) before these are reached.
 hipError_t launch_sdpa_bf16(const SdpaBf16Params& p, hipStream_t stream);

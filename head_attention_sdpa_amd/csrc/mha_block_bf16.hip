@@ -308,8 +308,7 @@ void gemm_bf16_ln_kernel(const GemmLnParams p) {
 hipError_t launch_pe_add_bf16(const PeAddParams& p, hipStream_t stream) {
   const int64_t threads = (int64_t)p.n * (p.d_model / 8);
   if (threads == 0 || p.batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(pe_add_bf16, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, p);
-  return hipGetLastError();
+  return launch_kernel(pe_add_bf16, dim3((unsigned)((threads + 255) / 256)), dim3(256), stream, p);
 }
 
 // 32-deep k stages in a 2-stage ring (136 KiB): one barrier per 16 MFMAs
@@ -320,13 +319,12 @@ hipError_t launch_gemm_bf16_ln(const GemmLnParams& p, hipStream_t stream) {
   if (p.M == 0) return hipSuccess;
   const dim3 grid((unsigned)((p.M + LBM - 1) / LBM)), block(64 * LWAVES);
   switch (p.N) {
-    case 256: hipLaunchKernelGGL((gemm_bf16_ln_kernel<1, LN_KS, LN_NS>), grid, block, 0, stream, p); break;
-    case 512: hipLaunchKernelGGL((gemm_bf16_ln_kernel<2, LN_KS, LN_NS>), grid, block, 0, stream, p); break;
-    case 768: hipLaunchKernelGGL((gemm_bf16_ln_kernel<3, LN_KS, LN_NS>), grid, block, 0, stream, p); break;
-    case 1024: hipLaunchKernelGGL((gemm_bf16_ln_kernel<4, LN_KS, LN_NS>), grid, block, 0, stream, p); break;
+    case 256: return launch_kernel(gemm_bf16_ln_kernel<1, LN_KS, LN_NS>, grid, block, stream, p);
+    case 512: return launch_kernel(gemm_bf16_ln_kernel<2, LN_KS, LN_NS>, grid, block, stream, p);
+    case 768: return launch_kernel(gemm_bf16_ln_kernel<3, LN_KS, LN_NS>, grid, block, stream, p);
+    case 1024: return launch_kernel(gemm_bf16_ln_kernel<4, LN_KS, LN_NS>, grid, block, stream, p);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace attn

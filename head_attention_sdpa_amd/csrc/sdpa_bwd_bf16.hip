@@ -453,15 +453,14 @@ hipError_t launch_sdpa_bwd_bf16(const SdpaBwdParams& p, hipStream_t stream) {
   // dQ first: it also writes the lse2 and -D planes the dK/dV kernel reads
   if (p.n_q > 0) {
     const int64_t grid = (int64_t)((p.n_q + 127) / 128) * bh;
-    hipLaunchKernelGGL(sdpa_bwd_dq<2>, dim3((unsigned)grid), dim3(256), 0, stream, p);
-    hipError_t e = hipGetLastError();
+    const hipError_t e = launch_kernel(sdpa_bwd_dq<2>, dim3((unsigned)grid), dim3(256), stream, p);
     if (e != hipSuccess) return e;
   }
   if (p.n_kv > 0) {
     const int64_t grid = (int64_t)((p.n_kv + 127) / 128) * bh;
-    hipLaunchKernelGGL(sdpa_bwd_dkdv<2>, dim3((unsigned)grid), dim3(256), 0, stream, p);
+    return launch_kernel(sdpa_bwd_dkdv<2>, dim3((unsigned)grid), dim3(256), stream, p);
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace attn

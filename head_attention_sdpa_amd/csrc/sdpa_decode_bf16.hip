@@ -271,12 +271,10 @@ void sdpa_decode_plan(int batch, int heads, int n_kv, int* chunk_tiles, int* n_c
 hipError_t launch_sdpa_decode_bf16(const SdpaDecodeParams& p, hipStream_t stream) {
   const int64_t bh = (int64_t)p.batch * p.heads;
   if (bh == 0 || p.n_q == 0) return hipSuccess;
-  hipLaunchKernelGGL(sdpa_decode_partial_bf16<kStages>, dim3((unsigned)(bh * p.n_chunks)), dim3(64), 0, stream,
-                     p);
-  hipError_t e = hipGetLastError();
+  const hipError_t e =
+      launch_kernel(sdpa_decode_partial_bf16<kStages>, dim3((unsigned)(bh * p.n_chunks)), dim3(64), stream, p);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(sdpa_decode_combine, dim3((unsigned)(bh * p.n_q)), dim3(64), 0, stream, p);
-  return hipGetLastError();
+  return launch_kernel(sdpa_decode_combine, dim3((unsigned)(bh * p.n_q)), dim3(64), stream, p);
 }
 
 }  // namespace attn

@@ -326,9 +326,8 @@ hipError_t launch_sdpa_bf16(const SdpaBf16Params& p_in, hipStream_t stream) {
   p.n_qblocks = (p.n_q + bm - 1) / bm;
   const int64_t grid = (int64_t)p.n_qblocks * p.batch * p.heads;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((sdpa_fwd_bf16_d64<kWaves, kStages, kWavesPerSimd>), dim3((unsigned)grid),
-                     dim3(64 * kWaves), 0, stream, p);
-  return hipGetLastError();
+  return launch_kernel(sdpa_fwd_bf16_d64<kWaves, kStages, kWavesPerSimd>, dim3((unsigned)grid),
+                       dim3(64 * kWaves), stream, p);
 }
 
 }  // namespace attn

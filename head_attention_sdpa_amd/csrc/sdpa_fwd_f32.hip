@@ -83,8 +83,7 @@ __global__ __launch_bounds__(64) void sdpa_fwd_f32_kernel(const SdpaF32Params p)
 hipError_t launch_sdpa_f32(const SdpaF32Params& p, hipStream_t stream) {
   if (p.n_q == 0 || p.batch == 0 || p.heads == 0) return hipSuccess;
   const dim3 grid((p.n_q + 63) / 64, p.heads, p.batch);
-  hipLaunchKernelGGL(sdpa_fwd_f32_kernel, grid, dim3(64), 0, stream, p);
-  return hipGetLastError();
+  return launch_kernel(sdpa_fwd_f32_kernel, grid, dim3(64), stream, p);
 }
 
 }  // namespace attn

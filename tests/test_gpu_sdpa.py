@@ -91,6 +91,8 @@ RAGGED = [
     dict(name="f32_small_d_causal_lengths", dtype="f32", B=2, H=2, nq=70, nkv=90, dk=5, dv=7,
          causal=True, lkv=[90, 33], lq=[70, 50]),
     dict(name="f32_d64_multiblock", dtype="f32", B=1, H=3, nq=130, nkv=77),
+    # 2048 (b, h) slices of 40 queries: a grid of 2048 one-block workgroups
+    dict(name="bf16_many_heads_causal", dtype="bf16", B=16, H=128, nq=40, nkv=40, causal=True),
 ]
 
 
@@ -100,6 +102,33 @@ def test_ragged_and_edge_cases(case):
     announce(f"sdpa {inp.name} shape={inp.shape} causal={inp.causal}")
     o, lse = run_gpu(inp)
     check_against_oracle(inp, o, lse)
+
+
+LONG = [
+    # one head of 65,536 positions, causal: 1,024 key tiles, 8 MiB per operand
+    dict(name="bf16_long_65536_causal", B=1, H=1, nq=65536, nkv=65536, causal=True),
+    # 2,048 queries over 49,152 cached keys of which 40,001 are valid
+    dict(name="bf16_long_cross_49152_len", B=1, H=1, nq=2048, nkv=49152, causal=False, lkv=[40001]),
+]
+
+
+@pytest.mark.parametrize("case", LONG, ids=[c["name"] for c in LONG])
+def test_long_sequence_sampled_rows(case):
+    """Long sequences: every query is computed on the GPU; 12 rows (first,
+    tile and block edges, middle, last) are checked against the oracle row
+    by row."""
+    inp = _case(dtype="bf16", cfg_id=97, **case)
+    announce(f"sdpa {inp.name} shape={inp.shape} causal={inp.causal}")
+    o, lse = run_gpu(inp)
+    n = inp.shape[2]
+    rows = np.unique(np.array([0, 1, 63, 64, 127, 128, 1000, n // 2 - 1, n // 2, n - 65, n - 64, n - 1]))
+    o_ref, lse_ref = oracle.sdpa_rows(inp.q, inp.k, inp.v, rows, scale=inp.scale, causal=inp.causal,
+                                      seqlens_kv=inp.seqlens_kv)
+    err = float(np.abs(o[0, 0, rows] - o_ref).max())
+    lse_err = float((np.abs(lse[0, 0, rows] - lse_ref) / np.maximum(1.0, np.abs(lse_ref))).max())
+    print(f"  {inp.name}: max|gpu-oracle| = {err:.3e}, lse rel {lse_err:.2e} over {len(rows)} rows", flush=True)
+    assert not np.isnan(o).any()
+    assert err <= TOL["bf16"] and lse_err <= LSE_TOL["bf16"]
 
 
 # ---------------------------------------------------------------------------
