@@ -31,7 +31,7 @@ STATUS = {0: "ATTN_OK", -1: "ATTN_E_INVALID", -2: "ATTN_E_UNSUPPORTED", -3: "ATT
 EXPORTS = ("attn_sdpa_fwd", "attn_sdpa_window_fwd", "attn_mha_workspace_bytes", "attn_mha_fwd", "attn_decode_workspace_bytes",
            "attn_decode_fwd", "attn_linear_fwd", "attn_mha_block_workspace_bytes", "attn_mha_block_fwd",
            "attn_sdpa_bwd_workspace_bytes", "attn_sdpa_bwd",
-           "attn_status_str", "attn_abi_version")
+           "attn_status_str", "attn_last_hip_error", "attn_hip_error_str", "attn_abi_version")
 
 
 class AttnError(RuntimeError):
@@ -47,14 +47,36 @@ class attn_strides(ctypes.Structure):
 _lib = None
 
 
+def hip_runtimes() -> list:
+    """Files of the HIP runtime (libamdhip64) mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({line.split()[-1] for line in f if "libamdhip64" in line})
+    except OSError:
+        return []
+
+
 def lib() -> ctypes.CDLL:
-    """The loaded C-ABI library (raises if it has not been built)."""
+    """The loaded C-ABI library (raises if it has not been built).
+
+    torch is imported first: the library's libamdhip64.so.7 dependency then
+    resolves to the HIP runtime torch has already loaded, so torch's memory
+    and streams and the library's kernels live in one runtime.  (Loaded the
+    other way round, the process holds two HIP and two HSA runtimes, one from
+    the ROCm installation and one shipped with torch, and the library's runtime
+    has reported hipErrorNoDevice at its first launch.)  Raises if more than
+    one HIP runtime is mapped after loading."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m head_attention_sdpa_amd.build` (or __graft_entry__.build())")
+        import torch  # noqa: F401  (its HIP runtime first, see above)
         L = ctypes.CDLL(LIB_PATH)
+        rts = hip_runtimes()
+        if len(rts) > 1:
+            raise ImportError(f"more than one HIP runtime is loaded in this process ({rts}): load torch "
+                              "before any other HIP library so that libattn_sdpa.so binds to torch's runtime")
         i, vp, sp = ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(attn_strides)
         L.attn_sdpa_fwd.argtypes = [i, i, i, i, i, i, i, vp, sp, vp, sp, vp, sp, vp, sp,
                                     ctypes.c_float, i, vp, vp, vp, vp]
@@ -89,6 +111,10 @@ def lib() -> ctypes.CDLL:
         L.attn_status_str.restype = ctypes.c_char_p
         L.attn_abi_version.argtypes = []
         L.attn_abi_version.restype = i
+        L.attn_last_hip_error.argtypes = []
+        L.attn_last_hip_error.restype = i
+        L.attn_hip_error_str.argtypes = [i]
+        L.attn_hip_error_str.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
@@ -99,7 +125,11 @@ def status_str(status: int) -> str:
 
 def _check(fn: str, rc: int):
     if rc != 0:
-        raise AttnError(fn, rc, status_str(rc))
+        msg = status_str(rc)
+        if rc == -5:  # ATTN_E_HIP: name the HIP error behind it
+            e = lib().attn_last_hip_error()
+            msg += f"; HIP error {e}: {lib().attn_hip_error_str(e).decode()}"
+        raise AttnError(fn, rc, msg)
 
 
 def _torch():

@@ -38,7 +38,14 @@ bool strides_aligned(const attn_strides& s, int64_t elems) {
   return s.b % elems == 0 && s.h % elems == 0 && s.n % elems == 0;
 }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_HIP; }
+// The HIP error behind the last ATTN_E_HIP of this host thread.
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return ATTN_OK;
+  g_last_hip_error = (int)e;
+  return ATTN_E_HIP;
+}
 
 // Shared checks of the SDPA arguments; fills the resolved strides and scale.
 int check_sdpa(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k, int d_v,
@@ -301,6 +308,10 @@ extern "C" {
 
 
 int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+
+const char* attn_hip_error_str(int hip_error) { return hipGetErrorString((hipError_t)hip_error); }
 
 const char* attn_status_str(int status) {
   switch (status) {

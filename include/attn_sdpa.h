@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 6
+#define ATTN_ABI_VERSION 7
 
 typedef void* attn_stream_t; /* hipStream_t */
 
@@ -176,6 +176,15 @@ int attn_mha_fwd(attn_dtype dt, int batch, int n_q, int n_kv, int d_model, int h
 
 /* Human-readable name of an attn_status value (static storage). */
 const char* attn_status_str(int status);
+
+/*
+ * attn_last_hip_error -- the hipError_t value behind the most recent
+ * ATTN_E_HIP returned on the calling host thread (0 if none so far); it is
+ * kept until the next ATTN_E_HIP on that thread.  attn_hip_error_str names
+ * such a value (HIP's own description, static storage).
+ */
+int attn_last_hip_error(void);
+const char* attn_hip_error_str(int hip_error);
 
 /*
  * attn_decode_workspace_bytes -- workspace that attn_decode_fwd needs for

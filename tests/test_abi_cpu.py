@@ -35,6 +35,25 @@ def test_abi_version_matches_header():
     assert attn.lib().attn_abi_version() == int(m.group(1))
 
 
+def test_one_hip_runtime_when_the_library_loads_first():
+    """Loading the library before anything imports torch still leaves one
+    HIP runtime in the process (torch's), checked in a fresh interpreter."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r); import head_attention_sdpa_amd as attn; attn.lib(); "
+            "print(repr(attn.hip_runtimes()))" % ROOT)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    runtimes = eval(out.stdout.strip().splitlines()[-1])
+    assert len(runtimes) == 1, runtimes
+
+
+def test_hip_error_reporting():
+    L = attn.lib()
+    assert L.attn_last_hip_error() == 0   # no ATTN_E_HIP on this thread so far
+    assert L.attn_hip_error_str(100).decode()   # HIP's name of hipErrorNoDevice
+
+
 def test_status_strings():
     for code in (0, -1, -2, -3, -4, -5):
         assert attn.status_str(code) and attn.status_str(code) != "unknown status"
