@@ -74,5 +74,30 @@ def build(extra: list[str] | None = None, verbose: bool = False, out: str | None
     return target
 
 
+DRIVER_SRC = os.path.join(ROOT, "tests", "c_abi", "sdpa_driver.cpp")
+DRIVER_PATH = os.path.join(ROOT, "tests", "c_abi", "sdpa_driver")
+
+
+def build_c_driver(verbose: bool = False) -> str:
+    """Compile the test program that calls the library through its C ABI
+    alone (tests/c_abi/sdpa_driver.cpp), linked against LIB_PATH with an
+    $ORIGIN-relative run path.  Always recompiles."""
+    cc = hipcc()
+    tmp = DRIVER_PATH + f".tmp{os.getpid()}"
+    rpath = "$ORIGIN/" + os.path.relpath(PKG, os.path.dirname(DRIVER_PATH))
+    cmd = [cc, f"--offload-arch={ARCH}", "-O2", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", os.path.join(ROOT, "include"), DRIVER_SRC, "-o", tmp,
+           "-L", PKG, "-lattn_sdpa", f"-Wl,-rpath,{rpath}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"driver build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, DRIVER_PATH)
+    if verbose:
+        print(f"built {DRIVER_PATH}")
+    return DRIVER_PATH
+
+
 if __name__ == "__main__":
     build(extra=sys.argv[1:], verbose=True)
+    build_c_driver(verbose=True)
