@@ -183,9 +183,10 @@ def test_decode_validation(kw, code):
 
 def test_decode_workspace_bytes():
     L = attn.lib()
-    # 16 x 16 heads, one query, 4096-key cache: 8 chunks of 8 tiles per (b, h);
-    # fp32 partial O (64 per row) and (m, l) per (b, h, chunk, query)
-    rows = 16 * 16 * 8 * 1
+    # 16 x 16 heads, one query, 4096-key cache: 4 chunks of 16 tiles per (b, h)
+    # (about 1024 workgroups); fp32 partial O (64 per row) and (m, l) per
+    # (b, h, chunk, query)
+    rows = 16 * 16 * 4 * 1
     assert L.attn_decode_workspace_bytes(1, 16, 16, 1, 4096, 64, 64) == rows * 64 * 4 + rows * 2 * 4
     assert L.attn_decode_workspace_bytes(0, 16, 16, 1, 4096, 64, 64) == 0   # f32 unsupported
     assert L.attn_decode_workspace_bytes(1, 16, 16, 33, 4096, 64, 64) == 0  # n_q > 32
