@@ -43,16 +43,26 @@ constexpr float LN2 = 0.69314718055994530942f;
 constexpr int kTargetGroups = 1024;
 constexpr int kStages = 2;
 
-template <int NS>
-__global__ __launch_bounds__(64) void sdpa_decode_partial_bf16(const SdpaDecodeParams p) {
-  static_assert(NS >= 2 && NS <= 6, "bad configuration");
+// W = 0: one wave per (b, h, chunk), which leaves its partial result in the
+// workspace for sdpa_decode_combine.  W = 1..4: one workgroup per (b, h) with
+// one wave per chunk (W = n_chunks); the waves merge their results through
+// LDS and wave 0 writes O and the log-sum-exp itself, so no second kernel
+// runs.  Either way each wave streams its chunk through a ring of its own and
+// waits only for its own copies.
+template <int NS, int W>
+__global__ __launch_bounds__(64 * (W > 0 ? W : 1)) void sdpa_decode_partial_bf16(const SdpaDecodeParams p) {
+  static_assert(NS >= 2 && NS <= 6 && W >= 0 && W <= 4, "bad configuration");
+  constexpr int NWAVE = W > 0 ? W : 1;
   constexpr int IPT = 16;  // DMA instructions per tile (8 K + 8 V row blocks of 8 rows)
-  __shared__ __attribute__((aligned(1024))) __bf16 smem[NS * 2 * TILE_E];
+  constexpr int RING_E = NS * 2 * TILE_E;  // one wave's ring
+  __shared__ __attribute__((aligned(1024))) __bf16 lds_all[NWAVE * RING_E];
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __bf16* const smem = lds_all + wave * RING_E;
   const int i32 = lane & 31, g = lane >> 5;
-  const int chunk = (int)(blockIdx.x % (unsigned)p.n_chunks);   // workgroup = bh * n_chunks + chunk
-  const int bh = (int)(blockIdx.x / (unsigned)p.n_chunks);
+  const int chunk = W > 0 ? wave : (int)(blockIdx.x % (unsigned)p.n_chunks);   // W = 0: workgroup = bh * n_chunks + chunk
+  const int bh = W > 0 ? (int)blockIdx.x : (int)(blockIdx.x / (unsigned)p.n_chunks);
   const int b = bh / p.heads, h = bh - b * p.heads;
 
   int Lkv = p.n_kv;
@@ -138,8 +148,9 @@ __global__ __launch_bounds__(64) void sdpa_decode_partial_bf16(const SdpaDecodeP
   for (int t = 0; t < nblk; ++t) {
     // tile t has landed once at most min(NS-2, nblk-1-t) newer tiles are in
     // flight; the wave's reads of tile t-1 are done before its stage refills
+    // (the ring is the wave's own: no barrier)
     wait_vmcnt_le<IPT>(min(NS - 2, nblk - 1 - t) * IPT);
-    barrier_lds();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (t + NS - 1 < nblk) issue_tile(t + NS - 1);
     const int key0 = kbeg + t * BN;
     const __bf16* Ks = smem + (t % NS) * 2 * TILE_E;
@@ -215,6 +226,80 @@ __global__ __launch_bounds__(64) void sdpa_decode_partial_bf16(const SdpaDecodeP
     l += rs;
   }
 
+  if constexpr (W > 0) {
+    // Merge the W chunks in LDS: waves 1..W-1 leave O (32 fp32 per lane, in
+    // the lane's accumulator layout), the shift m and the lane's sum l in
+    // their own ring; wave 0 scales each part by 2^(m_c - M), M the largest
+    // shift (a part without a legal key, m = -inf, weighs 0).
+    constexpr int CMB = 32 * 64 + 128;  // floats per wave
+    static_assert(CMB * 4 <= RING_E * 2, "merge area exceeds a ring");
+    if constexpr (W > 1) {
+      if (wave > 0) {
+        float* cmb = reinterpret_cast<float*>(smem);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          *reinterpret_cast<f32x4*>(cmb + 4 * (k * 64 + lane)) = f32x4{o0[4 * k], o0[4 * k + 1], o0[4 * k + 2], o0[4 * k + 3]};
+          *reinterpret_cast<f32x4*>(cmb + 4 * ((4 + k) * 64 + lane)) =
+              f32x4{o1[4 * k], o1[4 * k + 1], o1[4 * k + 2], o1[4 * k + 3]};
+        }
+        cmb[2048 + lane] = m;
+        cmb[2048 + 64 + lane] = l;
+      }
+      barrier_lds();
+      if (wave > 0) return;
+      float mm = m;
+#pragma unroll
+      for (int w = 1; w < W; ++w) mm = fmaxf(mm, reinterpret_cast<const float*>(lds_all + w * RING_E)[2048 + lane]);
+      const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+      l *= a0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        o0[r] *= a0;
+        o1[r] *= a0;
+      }
+#pragma unroll
+      for (int w = 1; w < W; ++w) {
+        const float* cmb = reinterpret_cast<const float*>(lds_all + w * RING_E);
+        const float mw = cmb[2048 + lane];
+        const float aw = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mm);
+        l = fmaf(aw, cmb[2048 + 64 + lane], l);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(cmb + 4 * (k * 64 + lane));
+          const f32x4 y = *reinterpret_cast<const f32x4*>(cmb + 4 * ((4 + k) * 64 + lane));
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            o0[4 * k + t] = fmaf(aw, x[t], o0[4 * k + t]);
+            o1[4 * k + t] = fmaf(aw, y[t], o1[4 * k + t]);
+          }
+        }
+      }
+      m = mm;
+    }
+    // O = O^T / l, rounded once to bf16; a query with no legal key gets zeros
+    // and lse = -inf.  Lane (query qi, half g) holds d = 8*rg + 4*g + 0..3
+    // (+32 in o1): 8-byte stores.
+    const float lt = sum_with_partner(l);
+    const bool valid = lt > 0.f;
+    const float inv = valid ? 1.f / lt : 0.f;
+    if (qi < p.n_q) {
+      __bf16* orow = reinterpret_cast<__bf16*>(p.o) + b * p.os_b + h * p.os_h + (int64_t)qi * p.os_n;
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        bf16x4 w0, w1;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          w0[t] = (__bf16)(o0[4 * rg + t] * inv);
+          w1[t] = (__bf16)(o1[4 * rg + t] * inv);
+        }
+        *reinterpret_cast<u32x2*>(orow + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, w0);
+        *reinterpret_cast<u32x2*>(orow + 32 + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, w1);
+      }
+      if (p.lse && g == 0) p.lse[(int64_t)bh * p.n_q + qi] = valid ? (m + __log2f(lt)) * LN2 : -INFINITY;
+    }
+    return;
+  }
+
   // partial result of this chunk (a chunk without keys leaves m = -inf, l = 0)
   const float lt = sum_with_partner(l);
   if (qi < p.n_q) {
@@ -274,8 +359,17 @@ void sdpa_decode_plan(int batch, int heads, int n_kv, int* chunk_tiles, int* n_c
 hipError_t launch_sdpa_decode_bf16(const SdpaDecodeParams& p, hipStream_t stream) {
   const int64_t bh = (int64_t)p.batch * p.heads;
   if (bh == 0 || p.n_q == 0) return hipSuccess;
+  // up to four chunks per (b, h): one workgroup per (b, h), merged in LDS
+  const dim3 g1((unsigned)bh);
+  switch (p.n_chunks) {
+    case 1: return launch_kernel(sdpa_decode_partial_bf16<kStages, 1>, g1, dim3(64), stream, p);
+    case 2: return launch_kernel(sdpa_decode_partial_bf16<kStages, 2>, g1, dim3(128), stream, p);
+    case 3: return launch_kernel(sdpa_decode_partial_bf16<kStages, 3>, g1, dim3(192), stream, p);
+    case 4: return launch_kernel(sdpa_decode_partial_bf16<kStages, 4>, g1, dim3(256), stream, p);
+    default: break;
+  }
   const hipError_t e =
-      launch_kernel(sdpa_decode_partial_bf16<kStages>, dim3((unsigned)(bh * p.n_chunks)), dim3(64), stream, p);
+      launch_kernel(sdpa_decode_partial_bf16<kStages, 0>, dim3((unsigned)(bh * p.n_chunks)), dim3(64), stream, p);
   if (e != hipSuccess) return e;
   return launch_kernel(sdpa_decode_combine, dim3((unsigned)(bh * p.n_q)), dim3(64), stream, p);
 }

@@ -216,9 +216,12 @@ size_t attn_decode_workspace_bytes(attn_dtype dt, int batch, int heads, int n_q,
  *               positions) or NULL.
  *   workspace   device memory of at least attn_decode_workspace_bytes(...)
  *               bytes, 256-byte aligned; contents on entry are ignored.
- * The keys are processed in chunks of whole 64-key tiles by independent
- * workgroups, and a second kernel merges the chunks.  o must not alias q, k,
- * v or the workspace.  Returns ATTN_OK or a negative attn_status.
+ * The keys are processed in chunks of whole 64-key tiles, one wave per chunk.
+ * With at most four chunks per (b, h) the chunks of a (b, h) run in one
+ * workgroup and merge in LDS (the workspace is then not written); otherwise
+ * they run as independent workgroups and a second kernel merges them through
+ * the workspace.  o must not alias q, k, v or the workspace.  Returns ATTN_OK
+ * or a negative attn_status.
  */
 int attn_decode_fwd(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k, int d_v,
                     const void* q, const attn_strides* sq, const void* k, const attn_strides* sk,

@@ -57,6 +57,12 @@ CASES = [
     dict(name="thirty_two_queries_full_tiles", B=2, H=2, n_q=32, n_kv=320, lo=320),
     dict(name="short_and_empty_sequences", B=4, H=1, n_q=2, n_kv=2048, L=[1, 0, 2, 2048]),
     dict(name="odd_queries_tail_tile", B=1, H=5, n_q=7, n_kv=4097, lo=4000),
+    # up to four chunks per (b, h) run as the waves of one workgroup, merged in LDS:
+    dict(name="merged_one_chunk_short_cache", B=2, H=3, n_q=5, n_kv=50, L=[50, 3]),
+    dict(name="merged_two_chunks", B=2, H=2, n_q=3, n_kv=100, L=[100, 65]),
+    dict(name="merged_three_chunks", B=1, H=3, n_q=7, n_kv=150, L=[150]),
+    dict(name="merged_four_chunks_empty_and_short", B=3, H=1, n_q=2, n_kv=256, L=[256, 0, 70]),
+    dict(name="merged_one_chunk_many_heads", B=64, H=16, n_q=1, n_kv=300, lo=1),
 ]
 
 
