@@ -7,18 +7,21 @@
 // up to and including their own position (the causal mask, aligned at the end
 // of the cache).  With few queries and a long cache the work is a stream over
 // K and V (256 bytes per key), so the keys of each (batch, head) are split
-// into chunks that run as independent single-wave workgroups:
+// into chunks, one wave per chunk; the wave's 32 lane columns are the (up to
+// 32) queries.  K/V tiles of 64 keys stream through an LDS-DMA ring of the
+// wave's own -- no barrier, only the wave's own vmcnt waits -- and each tile
+// runs the same transposed MFMA products and online softmax as the prefill
+// kernel.  A chunk ends with sum_j 2^(s_j - m) V_j, its shift m (log2 units)
+// and sum l, and the chunks are merged: O = sum_c 2^(m_c - M) O_c / L with
+// L = sum_c 2^(m_c - M) l_c, rounded to bf16 once, plus the log-sum-exp (the
+// shift cancels in O, rockcohen.cc section 3.2).
 //
-//   sdpa_decode_partial_bf16  workgroup = (batch*head, chunk), one wave; the
-//     wave's 32 lane columns are the (up to 32) queries.  K/V tiles of 64 keys
-//     stream through an LDS-DMA ring -- a single wave needs no
-//     barrier, only its own vmcnt waits -- and each tile runs the same
-//     transposed MFMA products and online softmax as the prefill kernel.  The
-//     chunk leaves sum_j 2^(s_j - m) V_j, its shift m (log2 units) and sum l.
-//   sdpa_decode_combine      one workgroup per (batch, head, query): rescales
-//     the chunks to the largest shift, O = sum_c 2^(m_c - M) O_c / L with
-//     L = sum_c 2^(m_c - M) l_c, rounds O to bf16 once, and writes the
-//     log-sum-exp.  The shift cancels in O (rockcohen.cc section 3.2).
+//   up to four chunks per (b, h): sdpa_decode_partial_bf16<NS, W> with one
+//     workgroup per (batch, head) and W = chunks waves, merged through LDS;
+//   more chunks: sdpa_decode_partial_bf16<NS, 0> with one single-wave
+//     workgroup per (batch, head, chunk), leaving its partial result in the
+//     workspace, then sdpa_decode_combine, one workgroup per (batch, head,
+//     query).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
