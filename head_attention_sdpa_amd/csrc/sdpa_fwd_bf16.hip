@@ -65,7 +65,10 @@ __device__ __forceinline__ void map_block(int bid, int bh_total, int nqb, int ca
 // There is no software pipeline inside a wave: the waves of a SIMD (WPE of
 // them, at most 512/WPE VGPRs each) interleave their vector and matrix work,
 // and the NS-stage ring is small enough that WPE workgroups share a CU's LDS.
-template <int NW, int NS, int WPE>
+// BAND compiles the restricted-attention bounds in; without it the mask has
+// one upper bound per lane (causal limit and key length), one compare per
+// score on the tiles that cross it.
+template <int NW, int NS, int WPE, bool BAND>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void sdpa_fwd_bf16_d64(const SdpaBf16Params p) {
   constexpr int BM = 32 * NW;
@@ -99,11 +102,12 @@ void sdpa_fwd_bf16_d64(const SdpaBf16Params p) {
     kv_end = min(kv_end, min(q0 + BM, Lq));
     wkv_end = min(wkv_end, min(qw0 + 32, Lq));
   }
-  if (p.window >= 0) {  // restricted attention: keys |i - j| <= window
-    kv_begin = max(0, q0 - p.window);
-    wkv_begin = max(0, qw0 - p.window);
-    kv_end = min(kv_end, min(q0 + BM, Lq) + p.window);
-    wkv_end = min(wkv_end, min(qw0 + 32, Lq) + p.window);
+  const int window = BAND ? p.window : -1;  // BAND: restricted attention, keys |i - j| <= window
+  if (BAND) {
+    kv_begin = max(0, q0 - window);
+    wkv_begin = max(0, qw0 - window);
+    kv_end = min(kv_end, min(q0 + BM, Lq) + window);
+    wkv_end = min(wkv_end, min(qw0 + 32, Lq) + window);
   }
   if (q0 >= Lq) kv_end = 0;
   if (qw0 >= Lq) wkv_end = 0;
@@ -205,17 +209,17 @@ void sdpa_fwd_bf16_d64(const SdpaBf16Params p) {
     // the wave (key length, diagonal, or the band |i - j| <= window): key
     // key0 + pos is legal iff thr_lo <= pos <= thr, where the lane's register
     // r holds pos = 8*(r/4) + 4*g + r%4 (+32 in sc1)
-    const int hi_w = min(Lkv - 1, min(p.causal ? qw0 : kFar, p.window >= 0 ? qw0 + p.window : kFar));
-    const int lo_w = p.window >= 0 ? qw0 + 31 - p.window : -kFar;
+    const int hi_w = min(Lkv - 1, min(p.causal ? qw0 : kFar, BAND ? qw0 + window : kFar));
+    const int lo_w = BAND ? qw0 + 31 - window : -kFar;
     if (key0 + BN - 1 > hi_w || key0 < lo_w) {
-      const int lim = min(Lkv - 1, min(p.causal ? qi : kFar, p.window >= 0 ? qi + p.window : kFar));
+      const int lim = min(Lkv - 1, min(p.causal ? qi : kFar, BAND ? qi + window : kFar));
       const int thr = lim - key0 - 4 * g;
-      const int thr_lo = (p.window >= 0 ? qi - p.window : -kFar) - key0 - 4 * g;
+      const int thr_lo = BAND ? qi - window - key0 - 4 * g : -kFar;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int pos = 8 * (r >> 2) + (r & 3);
-        if (pos > thr || pos < thr_lo) sc0[r] = -INFINITY;
-        if (pos + 32 > thr || pos + 32 < thr_lo) sc1[r] = -INFINITY;
+        if (pos > thr || (BAND && pos < thr_lo)) sc0[r] = -INFINITY;
+        if (pos + 32 > thr || (BAND && pos + 32 < thr_lo)) sc1[r] = -INFINITY;
       }
     }
     float mx = fmaxf(sc0[0], sc1[0]);
@@ -326,7 +330,10 @@ hipError_t launch_sdpa_bf16(const SdpaBf16Params& p_in, hipStream_t stream) {
   p.n_qblocks = (p.n_q + bm - 1) / bm;
   const int64_t grid = (int64_t)p.n_qblocks * p.batch * p.heads;
   if (grid == 0) return hipSuccess;
-  return launch_kernel(sdpa_fwd_bf16_d64<kWaves, kStages, kWavesPerSimd>, dim3((unsigned)grid),
+  if (p.window >= 0)
+    return launch_kernel(sdpa_fwd_bf16_d64<kWaves, kStages, kWavesPerSimd, true>, dim3((unsigned)grid),
+                         dim3(64 * kWaves), stream, p);
+  return launch_kernel(sdpa_fwd_bf16_d64<kWaves, kStages, kWavesPerSimd, false>, dim3((unsigned)grid),
                        dim3(64 * kWaves), stream, p);
 }
 
