@@ -295,7 +295,7 @@ void sdpa_fwd_bf16_d64(const SdpaBf16Params p) {
     *reinterpret_cast<u32x2*>(Os + i32 * D + 8 * ((4 + rg) ^ (i32 & 7)) + 4 * g) = __builtin_bit_cast(u32x2, w1);
   }
   if (p.lse && g == 0 && qi < p.n_q)
-    p.lse[((int64_t)b * p.heads + h) * p.n_q + qi] = valid ? (m + __log2f(lt)) * LN2 : -INFINITY;
+    store_out(p.lse + ((int64_t)b * p.heads + h) * p.n_q + qi, valid ? (m + __log2f(lt)) * LN2 : -INFINITY);
   __bf16* Ob = reinterpret_cast<__bf16*>(p.o) + b * p.os_b + h * p.os_h;
   const int c = lane & 7;
 #pragma unroll
@@ -303,7 +303,7 @@ void sdpa_fwd_bf16_d64(const SdpaBf16Params p) {
     const int r = 8 * i + (lane >> 3);
     if (qw0 + r < p.n_q) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(Os + r * D + 8 * (c ^ (r & 7)));
-      *reinterpret_cast<u32x4*>(Ob + (int64_t)(qw0 + r) * p.os_n + 8 * c) = v;
+      store_out(Ob + (int64_t)(qw0 + r) * p.os_n + 8 * c, v);
     }
   }
 }
