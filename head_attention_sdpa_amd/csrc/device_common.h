@@ -62,6 +62,14 @@ __device__ __forceinline__ void dma16(uint32_t voff, i32x4 rsrc, uint32_t lds_ad
                ::"v"(voff), "s"(rsrc), "s"(lds_addr) : "memory", "m0");
 }
 
+// The same copy with the non-temporal hint: the lines are marked for early
+// eviction from L2, for data read once that should not displace data that
+// other workgroups are about to read again.
+__device__ __forceinline__ void dma16_nt(uint32_t voff, i32x4 rsrc, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+               ::"v"(voff), "s"(rsrc), "s"(lds_addr) : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");

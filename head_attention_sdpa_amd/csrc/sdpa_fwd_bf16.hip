@@ -151,13 +151,21 @@ void sdpa_fwd_bf16_d64(const SdpaBf16Params p) {
   // after the barrier of the first iteration, when every wave has read its Q
   // fragments.  Q goes first, so once at most (prologue tiles) DMAs are in
   // flight Q has landed, while the prologue tiles may still be on their way.
+  // With restricted attention each K/V tile also serves the neighbouring
+  // query blocks on this XCD, so Q (read once) is copied with the
+  // non-temporal hint and does not displace them in L2 (measured: window
+  // 44.8 -> 42.4 us; with full attention the hint cost up to 3% on the
+  // decoder, so there Q is copied plainly).
   const __bf16* Qs = smem + (NS - 1) * 2 * TILE_E + wave * 32 * D;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 8 * i + (lane >> 3);
     const int chunk = (lane & 7) ^ swz_k(r);
     const uint32_t voff = (uint32_t)(((int64_t)(qw0 + r) * p.qs_n + chunk * 8) * 2);
-    dma16(voff, rs_q, lds_addr(Qs + 8 * i * D));
+    if (BAND)
+      dma16_nt(voff, rs_q, lds_addr(Qs + 8 * i * D));
+    else
+      dma16(voff, rs_q, lds_addr(Qs + 8 * i * D));
   }
   int prologue = 0;
 #pragma unroll
