@@ -116,9 +116,9 @@ __device__ __forceinline__ float sum_with_partner(float x) {
 // partial-row stores of the backward and decode kernels and for the GEMM
 // outputs they were slower, so those keep plain stores.  The stores are
 // issued from inline assembly, so the compiler does not count them among its
-// own memory operations; vector memory operations complete in issue order,
-// so its waits stay correct.  Only for final results that the same kernel
-// does not read back.
+// own memory operations: a kernel issues them after its last global load, so
+// that no wait the compiler inserts has to cover them, and only for final
+// results that the same kernel does not read back.
 __device__ __forceinline__ void store_out(void* p, u32x4 v) {
   asm volatile("global_store_dwordx4 %0, %1, off nt sc1" ::"v"(p), "v"(v) : "memory");
 }
