@@ -118,9 +118,12 @@ __device__ __forceinline__ float sum_with_partner(float x) {
 // issued from inline assembly, so the compiler does not count them among its
 // own memory operations: a kernel issues them after its last global load, so
 // that no wait the compiler inserts has to cover them, and only for final
-// results that the same kernel does not read back.
+// results that the same kernel does not read back.  The compiler's hazard
+// checks do not see into the assembly either: a store of more than 64 bits
+// must be followed by two wait states before a vector ALU instruction may
+// overwrite its data registers, so the 16-byte form carries its own s_nop.
 __device__ __forceinline__ void store_out(void* p, u32x4 v) {
-  asm volatile("global_store_dwordx4 %0, %1, off nt sc1" ::"v"(p), "v"(v) : "memory");
+  asm volatile("global_store_dwordx4 %0, %1, off nt sc1\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
 }
 __device__ __forceinline__ void store_out(void* p, u32x2 v) {
   asm volatile("global_store_dwordx2 %0, %1, off nt sc1" ::"v"(p), "v"(v) : "memory");

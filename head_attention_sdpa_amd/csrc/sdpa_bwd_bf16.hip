@@ -98,6 +98,7 @@ void sdpa_bwd_dkdv(const SdpaBwdParams p) {
   constexpr int STAGE_E = 2 * TILE_E;      // Q tile, dO tile
   constexpr int IPT = 4;                   // Q/dO DMA instructions per wave per stage (+1 for waves 0, 1)
   static_assert(NS >= 2 && NS <= 4, "bad configuration");
+  static_assert(NS * STAGE_E >= 8 * 32 * D, "the dK and dV blocks must fit the ring");
   __shared__ __attribute__((aligned(1024))) __bf16 smem[NS * STAGE_E];
   __shared__ __attribute__((aligned(1024))) float lds_l2[NS][256];   // per stage: lse2 of queries q0..q0+255
   __shared__ __attribute__((aligned(1024))) float lds_nd[NS][256];   // per stage: -D of the same queries
@@ -255,30 +256,50 @@ void sdpa_bwd_dkdv(const SdpaBwdParams p) {
   }
 
   // dK = scale dK^T, dV = dV^T, one rounding to bf16; register r of block cb
-  // holds d = 32*cb + 8*(r/4) + 4*g + r%4 of key kj
-  if (kj < p.n_kv) {
-    const bool kvalid = kj < Lkv;   // the columns of keys past L_kv hold no gradient (maybe inf/NaN)
-    __bf16* dkrow = reinterpret_cast<__bf16*>(p.dk) + b * p.dks_b + h * p.dks_h + (int64_t)kj * p.dks_n;
-    __bf16* dvrow = reinterpret_cast<__bf16*>(p.dv) + b * p.dvs_b + h * p.dvs_h + (int64_t)kj * p.dvs_n;
+  // holds d = 32*cb + 8*(r/4) + 4*g + r%4 of key kj.  Each wave stages its
+  // 32 x 64 blocks of dK and dV in its own 4 KiB pieces of the (now idle)
+  // ring -- 16-byte chunk c of row r at position c ^ (r & 7) -- and writes
+  // them out as whole 128-byte rows with write-through stores.
+  const bool kvalid = kj < Lkv;   // the columns of keys past L_kv hold no gradient (maybe inf/NaN)
+  barrier_lds();                  // every wave is past its last read of the ring
+  __bf16* dKs = smem + wave * 32 * D;
+  __bf16* dVs = smem + (4 + wave) * 32 * D;
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      bf16x4 a0, a1, b0, b1;
+  for (int rg = 0; rg < 4; ++rg) {
+    bf16x4 a0, a1;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        a0[t] = (__bf16)(kvalid ? dk0[4 * rg + t] * p.scale : 0.f);
-        a1[t] = (__bf16)(kvalid ? dk1[4 * rg + t] * p.scale : 0.f);
-        b0[t] = (__bf16)(kvalid ? dv0[4 * rg + t] : 0.f);
-        b1[t] = (__bf16)(kvalid ? dv1[4 * rg + t] : 0.f);
-      }
-      *reinterpret_cast<u32x2*>(dkrow + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, a0);
-      *reinterpret_cast<u32x2*>(dkrow + 32 + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, a1);
-      *reinterpret_cast<u32x2*>(dvrow + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, b0);
-      *reinterpret_cast<u32x2*>(dvrow + 32 + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, b1);
+    for (int t = 0; t < 4; ++t) {
+      a0[t] = (__bf16)(kvalid ? dk0[4 * rg + t] * p.scale : 0.f);
+      a1[t] = (__bf16)(kvalid ? dk1[4 * rg + t] * p.scale : 0.f);
+    }
+    *reinterpret_cast<u32x2*>(dKs + i32 * D + 8 * (rg ^ (i32 & 7)) + 4 * g) = __builtin_bit_cast(u32x2, a0);
+    *reinterpret_cast<u32x2*>(dKs + i32 * D + 8 * ((4 + rg) ^ (i32 & 7)) + 4 * g) = __builtin_bit_cast(u32x2, a1);
+  }
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg) {
+    bf16x4 b0, b1;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      b0[t] = (__bf16)(kvalid ? dv0[4 * rg + t] : 0.f);
+      b1[t] = (__bf16)(kvalid ? dv1[4 * rg + t] : 0.f);
+    }
+    *reinterpret_cast<u32x2*>(dVs + i32 * D + 8 * (rg ^ (i32 & 7)) + 4 * g) = __builtin_bit_cast(u32x2, b0);
+    *reinterpret_cast<u32x2*>(dVs + i32 * D + 8 * ((4 + rg) ^ (i32 & 7)) + 4 * g) = __builtin_bit_cast(u32x2, b1);
+  }
+  __bf16* dKb = reinterpret_cast<__bf16*>(p.dk) + b * p.dks_b + h * p.dks_h;
+  __bf16* dVb = reinterpret_cast<__bf16*>(p.dv) + b * p.dvs_b + h * p.dvs_h;
+  const int c = lane & 7;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * i + (lane >> 3);
+    if (kw0 + r < p.n_kv) {
+      const int pos = 8 * (c ^ (r & 7));
+      store_out(dKb + (int64_t)(kw0 + r) * p.dks_n + 8 * c, *reinterpret_cast<const u32x4*>(dKs + r * D + pos));
+      store_out(dVb + (int64_t)(kw0 + r) * p.dvs_n + 8 * c, *reinterpret_cast<const u32x4*>(dVs + r * D + pos));
     }
   }
 }
 
-// ---------------------------------------------------------------------------
 template <int NS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void sdpa_bwd_dq(const SdpaBwdParams p) {
@@ -286,6 +307,7 @@ void sdpa_bwd_dq(const SdpaBwdParams p) {
   constexpr int STAGE_E = 2 * TILE_E;      // K tile, V tile
   constexpr int IPT = 4;
   static_assert(NS >= 2 && NS <= 4, "bad configuration");
+  static_assert(NS * STAGE_E >= 4 * 32 * D, "the dQ blocks must fit the ring");
   __shared__ __attribute__((aligned(1024))) __bf16 smem[NS * STAGE_E];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -428,20 +450,29 @@ void sdpa_bwd_dq(const SdpaBwdParams p) {
     }
   }
 
-  // dQ = scale dQ^T, one rounding to bf16 (rows past the length are zeros)
-  if (qi < p.n_q) {
-    __bf16* dqrow = reinterpret_cast<__bf16*>(p.dq) + b * p.dqs_b + h * p.dqs_h + (int64_t)qi * p.dqs_n;
+  // dQ = scale dQ^T, one rounding to bf16 (rows past the length are zeros),
+  // staged per wave in the idle ring and written as whole rows as above
+  barrier_lds();   // every wave is past its last read of the ring
+  __bf16* dQs = smem + wave * 32 * D;
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      bf16x4 a0, a1;
+  for (int rg = 0; rg < 4; ++rg) {
+    bf16x4 a0, a1;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        a0[t] = (__bf16)(dq0[4 * rg + t] * p.scale);
-        a1[t] = (__bf16)(dq1[4 * rg + t] * p.scale);
-      }
-      *reinterpret_cast<u32x2*>(dqrow + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, a0);
-      *reinterpret_cast<u32x2*>(dqrow + 32 + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, a1);
+    for (int t = 0; t < 4; ++t) {
+      a0[t] = (__bf16)(dq0[4 * rg + t] * p.scale);
+      a1[t] = (__bf16)(dq1[4 * rg + t] * p.scale);
     }
+    *reinterpret_cast<u32x2*>(dQs + i32 * D + 8 * (rg ^ (i32 & 7)) + 4 * g) = __builtin_bit_cast(u32x2, a0);
+    *reinterpret_cast<u32x2*>(dQs + i32 * D + 8 * ((4 + rg) ^ (i32 & 7)) + 4 * g) = __builtin_bit_cast(u32x2, a1);
+  }
+  __bf16* dQb = reinterpret_cast<__bf16*>(p.dq) + b * p.dqs_b + h * p.dqs_h;
+  const int c = lane & 7;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * i + (lane >> 3);
+    if (qw0 + r < p.n_q)
+      store_out(dQb + (int64_t)(qw0 + r) * p.dqs_n + 8 * c,
+                *reinterpret_cast<const u32x4*>(dQs + r * D + 8 * (c ^ (r & 7))));
   }
 }
 
