@@ -56,9 +56,11 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 }
 
 // One global -> LDS copy: this lane's 16 bytes at buffer offset voff land at
-// LDS address lds_addr + 16 * lane.
+// LDS address lds_addr + 16 * lane.  The wait state between the write of M0
+// and the copy that reads it is the one the GFX9 family asks for (the
+// compiler does not look into the assembly to add it).
 __device__ __forceinline__ void dma16(uint32_t voff, i32x4 rsrc, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                ::"v"(voff), "s"(rsrc), "s"(lds_addr) : "memory", "m0");
 }
 
@@ -66,7 +68,7 @@ __device__ __forceinline__ void dma16(uint32_t voff, i32x4 rsrc, uint32_t lds_ad
 // eviction from L2, for data read once that should not displace data that
 // other workgroups are about to read again.
 __device__ __forceinline__ void dma16_nt(uint32_t voff, i32x4 rsrc, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
                ::"v"(voff), "s"(rsrc), "s"(lds_addr) : "memory", "m0");
 }
 
