@@ -48,11 +48,22 @@ __device__ __forceinline__ bf16x4 tr_read(const __bf16* lds_elem) {
 // Raw buffer descriptor: 48-bit base, stride 0, range in bytes; reads at or
 // past the range return zeros.  The descriptor must live in scalar registers:
 // every input is wave-uniform, and readfirstlane says so to the compiler.
+// When the compiler computes a word with a vector instruction it moves it to
+// a scalar register with v_readfirstlane, and a buffer instruction that reads
+// a scalar register written by a vector instruction needs five wait states
+// first (GFX9 family).  The copies below are issued from inline assembly,
+// where the compiler cannot add them, so every word is passed through a
+// scalar move: its last writer is then a scalar instruction.
+__device__ __forceinline__ int sgpr_word(int x) {
+  int y;
+  asm volatile("s_mov_b32 %0, %1" : "=s"(y) : "s"(x));
+  return y;
+}
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
-               __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff),
-               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+  return i32x4{sgpr_word(__builtin_amdgcn_readfirstlane((int)(uint32_t)a)),
+               sgpr_word(__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff)),
+               sgpr_word(__builtin_amdgcn_readfirstlane((int)bytes)), 0x00020000};
 }
 
 // One global -> LDS copy: this lane's 16 bytes at buffer offset voff land at
