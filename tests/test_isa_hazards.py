@@ -10,7 +10,11 @@ instructions:
   2. an LDS copy (buffer_load ... lds) is not the instruction right after the
      write of M0 that it reads;
   3. no vector instruction overwrites the data registers of a store of more
-     than 64 bits in the two instructions after it.
+     than 64 bits in the two instructions after it;
+
+and the ordering rule of the write-through stores (`nt sc1`), whose vector
+memory counts the compiler does not track: in each kernel no global or
+buffer load follows them.
 """
 import concurrent.futures as cf
 import os
@@ -64,8 +68,15 @@ _NO_SCALAR_DEST = ("s_cmp", "s_bitcmp", "s_cbranch", "s_waitcnt", "s_nop", "s_ba
 def hazards(instrs):
     """List of (rule, index, text) for every violation in one instruction stream."""
     found = []
+    after_asm_store = False
     for i, ins in enumerate(instrs):
         op = ins.split()[0]
+        if op == "s_endpgm":
+            after_asm_store = False
+        if re.match(r"(global|buffer)_store\w*\b.*\bnt sc1\b", ins):
+            after_asm_store = True
+        elif after_asm_store and re.match(r"(global|buffer)_load", op):
+            found.append(("load after a write-through store", i, ins))
         if op.startswith("buffer_"):
             # the latest writer of each scalar operand among the five
             # instructions before must not be a vector instruction
@@ -107,6 +118,9 @@ def test_rules_catch_the_patterns():
           "v_or_b32_e32 v4, 16, v134"]
     assert [h[0] for h in hazards(st)] == ["store data overwritten within two instructions"]
     assert hazards(st[:1] + ["s_nop 1"] + st[1:]) == []
+    ld = ["global_store_dword v[2:3], v1, off nt sc1", "global_load_dword v5, v[6:7], off", "s_endpgm"]
+    assert [h[0] for h in hazards(ld)] == ["load after a write-through store"]
+    assert hazards(ld[:1] + ["s_endpgm"] + ld[1:]) == []
 
 
 @pytest.mark.skipif(shutil.which(hip_build.hipcc()) is None and not os.path.exists(hip_build.hipcc()),
