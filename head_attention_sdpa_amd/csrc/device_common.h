@@ -1,14 +1,15 @@
 // Device helpers shared by the library's gfx950 kernels (not installed).
 //
 //   - vector types of the MFMA operands and accumulators;
-//   - the MFMA 32x32x16 bf16 product and the transposed LDS read;
+//   - the MFMA 32x32x16 and 16x16x32 bf16 products and the transposed LDS
+//     read;
 //   - global -> LDS copies (LDS DMA): 16 bytes per lane, lane i of the wave
 //     lands at M0 + 16*i, addressed through a raw buffer descriptor whose
 //     range makes reads past it return zeros.  They are issued from inline
 //     assembly and waited for with explicit vmcnt counts, so the compiler
 //     never inserts its own conservative "all DMA done" waits in front of
 //     LDS reads, which would drain a prefetch ring every iteration;
-//   - cross-lane reductions between lanes l and l^32.
+//   - cross-lane reductions between lanes l and l^32 or l^16.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -34,6 +35,14 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 //   C[32 x 32]: lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4, col l%32
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x32_bf16 (lane layouts checked by a probe on gfx950):
+//   A[16 x 32]: lane l holds row l%16, k = 8*(l/16) + 0..7
+//   B[32 x 16]: lane l holds col l%16, k = 8*(l/16) + 0..7
+//   C[16 x 16]: lane l, register r holds row 4*(l/16) + r, col l%16
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // ds_read_b64_tr_b16: per group of 16 lanes where lane k points at 4 values
@@ -112,6 +121,17 @@ __device__ __forceinline__ float max_with_partner(float x) {
   uint32_t u = __float_as_uint(x);
   auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// The same with lane l^16 (gfx950 v_permlane16_swap).
+__device__ __forceinline__ float max_with_lane16(float x) {
+  uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_lane16(float x) {
+  uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 __device__ __forceinline__ float sum_with_partner(float x) {
   uint32_t u = __float_as_uint(x);

@@ -156,7 +156,10 @@ hipError_t launch_pe_add_bf16(const PeAddParams& p, hipStream_t stream);
 hipError_t launch_gemm_bf16_ln(const GemmLnParams& p, hipStream_t stream);
 bool gemm_bf16_main_supported(const GemmBf16Params& p);   // shapes the fast kernel takes
 
-// Queries per workgroup of the bf16 SDPA kernel chosen for these sizes.
+// Queries per workgroup of the streaming bf16 SDPA kernel.
 int sdpa_bf16_block_m(int batch, int heads, int n_q);
+// True when the bf16 SDPA runs one workgroup per (batch, head) with all keys
+// resident in LDS (short sequences, no band).
+bool sdpa_bf16_resident(int n_q, int n_kv, int window);
 
 }  // namespace attn

@@ -104,6 +104,33 @@ def test_ragged_and_edge_cases(case):
     check_against_oracle(inp, o, lse)
 
 
+# Shapes on both sides of the short-sequence kernel's limits (one workgroup per
+# (batch, head) when n_q <= 256 and n_kv <= 384, eight waves up to n_q = 128,
+# 2/4/6 resident key tiles): masks, lengths that leave a single active group
+# of 16 queries, heads with no key, and causal masks with n_q != n_kv.
+RESIDENT_EDGES = [
+    dict(name="res_nq256_nkv384_len", B=2, H=3, nq=256, nkv=384, lkv=[384, 200]),
+    dict(name="stream_nq257_nkv384", B=1, H=2, nq=257, nkv=384),
+    dict(name="stream_nq128_nkv385", B=1, H=2, nq=128, nkv=385),
+    dict(name="res_nq129_nkv130_causal", B=2, H=2, nq=129, nkv=130, causal=True),
+    dict(name="res_nq128_nkv128_causal_len", B=3, H=2, nq=128, nkv=128, causal=True, lq=[128, 77, 1],
+         lkv=[128, 128, 60]),
+    dict(name="res_nq16_causal_len_zero", B=3, H=2, nq=16, nkv=16, causal=True, lq=[16, 7, 0]),
+    dict(name="res_causal_nq_lt_nkv", B=1, H=3, nq=100, nkv=300, causal=True),
+    dict(name="res_causal_nq_gt_nkv", B=1, H=3, nq=250, nkv=70, causal=True),
+    dict(name="res_one_active_group", B=2, H=2, nq=256, nkv=384, lq=[10, 256], lkv=[384, 1]),
+    dict(name="res_no_keys_in_one_head", B=2, H=2, nq=200, nkv=64, causal=True, lq=[200, 200], lkv=[0, 64]),
+]
+
+
+@pytest.mark.parametrize("case", RESIDENT_EDGES, ids=[c["name"] for c in RESIDENT_EDGES])
+def test_short_sequence_kernel_edges(case):
+    inp = _case(dtype="bf16", cfg_id=89, **case)
+    announce(f"sdpa {inp.name} shape={inp.shape} causal={inp.causal}")
+    o, lse = run_gpu(inp)
+    check_against_oracle(inp, o, lse)
+
+
 LONG = [
     # one head of 65,536 positions, causal: 1,024 key tiles, 8 MiB per operand
     dict(name="bf16_long_65536_causal", B=1, H=1, nq=65536, nkv=65536, causal=True),

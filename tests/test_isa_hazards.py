@@ -12,9 +12,16 @@ instructions:
   3. no vector instruction overwrites the data registers of a store of more
      than 64 bits in the two instructions after it;
 
-and the ordering rule of the write-through stores (`nt sc1`), whose vector
-memory counts the compiler does not track: in each kernel no global or
-buffer load follows them.
+and the ordering rule of the write-through stores (`nt sc1`), which the
+compiler does not count among its vector memory operations: on no path from
+such a store is there a load that returns data to registers (the compiler
+would wait for it with a count that misses the store), and every vector
+memory wait on such a path is vmcnt(0), which no uncounted store can
+confuse (the LDS copies after a store are only waited for that way).
+
+"Before" and "after" follow the control flow: the instructions before a
+branch target include the branches that jump to it (loop back-edges too),
+and the instructions after a branch include its target.
 """
 import concurrent.futures as cf
 import os
@@ -48,16 +55,44 @@ def _operands(instr):
     return [o.strip().split()[0] for o in parts[1].split(",") if o.strip()] if len(parts) > 1 else []
 
 
-def _instructions(asm_text):
-    """Instructions of the assembly in order (labels, directives and comments
-    dropped; the lines of an inline-assembly block are instructions too)."""
-    out = []
-    for line in asm_text.splitlines():
-        t = line.strip()
-        if not t or t.startswith((";", ".", "//")) or t.endswith(":"):
+def _program(lines):
+    """Instructions in order plus the label -> instruction index map.  Labels,
+    directives and comments are dropped; the lines of an inline-assembly
+    block are instructions too.  Each kernel ends at s_endpgm."""
+    instrs, labels = [], {}
+    for line in lines:
+        t = line.split(";")[0].split("//")[0].strip()
+        if not t:
             continue
-        out.append(t.split(";")[0].strip())
-    return out
+        if t.endswith(":"):
+            labels[t[:-1]] = len(instrs)
+            continue
+        if t.startswith("."):
+            continue
+        instrs.append(t)
+    return instrs, labels
+
+
+_UNCONDITIONAL = ("s_branch", "s_endpgm", "s_setpc_b64")
+
+
+def _edges(instrs, labels):
+    """Successor and predecessor lists of every instruction."""
+    succ = [[] for _ in instrs]
+    for i, ins in enumerate(instrs):
+        op = ins.split()[0]
+        if op not in _UNCONDITIONAL and i + 1 < len(instrs):
+            succ[i].append(i + 1)
+        if op == "s_branch" or op.startswith("s_cbranch"):
+            target = ins.split()[1]
+            assert target in labels, f"branch to an unknown label: {ins}"
+            succ[i].append(labels[target])
+        assert op != "s_setpc_b64", "indirect jump: the checker cannot follow it"
+    pred = [[] for _ in instrs]
+    for i, ss in enumerate(succ):
+        for j in ss:
+            pred[j].append(i)
+    return succ, pred
 
 
 # scalar instructions whose first operand is not a destination
@@ -65,62 +100,124 @@ _NO_SCALAR_DEST = ("s_cmp", "s_bitcmp", "s_cbranch", "s_waitcnt", "s_nop", "s_ba
                    "s_sleep", "s_branch", "s_endpgm")
 
 
-def hazards(instrs):
-    """List of (rule, index, text) for every violation in one instruction stream."""
+def _vector_writer_within(instrs, pred, i, pending, depth):
+    """Does a vector instruction write one of `pending` (scalar registers) on
+    some path of at most `depth` instructions ending right before i, with no
+    scalar instruction rewriting it in between?"""
+    for j in pred[i]:
+        prev = instrs[j]
+        ops = _operands(prev)
+        left = pending
+        if ops and not prev.split()[0].startswith(_NO_SCALAR_DEST):
+            written = _sregs(ops[0]) & pending
+            if written and prev.startswith("v_"):
+                return True
+            left = pending - written
+        if left and depth > 1 and _vector_writer_within(instrs, pred, j, left, depth - 1):
+            return True
+    return False
+
+
+def _store_data_overwritten(instrs, succ, i, data, depth):
+    for j in succ[i]:
+        nxt = instrs[j]
+        if nxt.startswith("v_") and _operands(nxt) and _vregs(_operands(nxt)[0]) & data:
+            return True
+        if depth > 1 and _store_data_overwritten(instrs, succ, j, data, depth - 1):
+            return True
+    return False
+
+
+def _write_through(ins):
+    return re.match(r"(global|buffer)_store\w*\b.*\bnt sc1\b", ins) is not None
+
+
+def hazards(lines):
+    """List of (rule, index, text) for every violation in a stream of
+    assembly lines (instructions and labels)."""
+    instrs, labels = _program(lines)
+    succ, pred = _edges(instrs, labels)
     found = []
-    after_asm_store = False
+    # instructions reachable from a write-through store
+    after_store, todo = set(), [i for i, ins in enumerate(instrs) if _write_through(ins)]
+    while todo:
+        i = todo.pop()
+        for j in succ[i]:
+            if j not in after_store:
+                after_store.add(j)
+                todo.append(j)
     for i, ins in enumerate(instrs):
         op = ins.split()[0]
-        if op == "s_endpgm":
-            after_asm_store = False
-        if re.match(r"(global|buffer)_store\w*\b.*\bnt sc1\b", ins):
-            after_asm_store = True
-        elif after_asm_store and re.match(r"(global|buffer)_load", op):
-            found.append(("load after a write-through store", i, ins))
+        if i in after_store:
+            if re.match(r"(global|buffer)_load", op) and not ins.rstrip().endswith(" lds"):
+                found.append(("register load after a write-through store", i, ins))
+            m = re.search(r"vmcnt\((\d+)\)", ins)
+            if op == "s_waitcnt" and m and int(m.group(1)) != 0:
+                found.append(("counted vector memory wait after a write-through store", i, ins))
         if op.startswith("buffer_"):
-            # the latest writer of each scalar operand among the five
-            # instructions before must not be a vector instruction
             pending = set().union(*(_sregs(o) for o in _operands(ins)))
-            for j in range(i - 1, max(-1, i - 6), -1):
-                prev = instrs[j]
-                ops = _operands(prev)
-                if not ops or prev.split()[0].startswith(_NO_SCALAR_DEST):
-                    continue
-                written = _sregs(ops[0]) & pending
-                if written and prev.startswith("v_"):
-                    found.append(("vector-written scalar register read by a buffer instruction", i, ins))
-                    break
-                pending -= written
-            if ins.rstrip().endswith(" lds") and i > 0 and re.match(r"s_\w+\s+m0\b", instrs[i - 1]):
+            if pending and _vector_writer_within(instrs, pred, i, pending, 5):
+                found.append(("vector-written scalar register read by a buffer instruction", i, ins))
+            if ins.rstrip().endswith(" lds") and any(re.match(r"s_\w+\s+m0\b", instrs[j]) for j in pred[i]):
                 found.append(("M0 written right before an LDS copy", i, ins))
         if re.match(r"(global|buffer)_store_dword(x3|x4)\b", op):
             ops = _operands(ins)
             data = _vregs(ops[1]) if op.startswith("global") else _vregs(ops[0])
-            for j in range(i + 1, min(len(instrs), i + 3)):
-                nxt = instrs[j]
-                if nxt.startswith("v_") and _operands(nxt) and _vregs(_operands(nxt)[0]) & data:
-                    found.append(("store data overwritten within two instructions", i, ins))
+            if _store_data_overwritten(instrs, succ, i, data, 2):
+                found.append(("store data overwritten within two instructions", i, ins))
     return found
+
+
+def _rules(lines):
+    return [h[0] for h in hazards(lines)]
 
 
 def test_rules_catch_the_patterns():
     """The checker itself: each rule fires on a minimal bad sequence and not on
-    the fixed one."""
+    the fixed one, along straight-line code and across branches."""
     bad = ["v_readfirstlane_b32 s26, v45", "s_mov_b32 m0, s3", "s_nop 0",
            "buffer_load_dwordx4 v35, s[24:27], 0 offen lds"]
-    assert [h[0] for h in hazards(bad)] == ["vector-written scalar register read by a buffer instruction"]
+    assert _rules(bad) == ["vector-written scalar register read by a buffer instruction"]
     ok = ["v_readfirstlane_b32 s26, v45", "s_mov_b32 s26, s26", "s_mov_b32 m0, s3", "s_nop 0",
           "buffer_load_dwordx4 v35, s[24:27], 0 offen lds"]
-    assert hazards(ok) == []
-    assert [h[0] for h in hazards(["s_mov_b32 m0, s3", "buffer_load_dwordx4 v1, s[4:7], 0 offen lds"])] == \
+    assert _rules(ok) == []
+    # loop-carried: the vector write sits at the latch, the copy at the loop head
+    loop = [".LBB0_1:", "s_mov_b32 m0, s3", "s_nop 0", "buffer_load_dwordx4 v35, s[24:27], 0 offen lds",
+            "s_add_i32 s4, s4, 1", "s_cmp_lt_i32 s4, 8", "v_readfirstlane_b32 s26, v45",
+            "s_cbranch_scc1 .LBB0_1", "s_endpgm"]
+    assert _rules(loop) == ["vector-written scalar register read by a buffer instruction"]
+    # the write at the end of an if-block, the copy at the join
+    join = ["s_cbranch_scc0 .LBB0_2", "v_readfirstlane_b32 s26, v45", ".LBB0_2:", "s_mov_b32 m0, s3",
+            "s_nop 0", "buffer_load_dwordx4 v35, s[24:27], 0 offen lds", "s_endpgm"]
+    assert _rules(join) == ["vector-written scalar register read by a buffer instruction"]
+    assert _rules(["s_mov_b32 m0, s3", "buffer_load_dwordx4 v1, s[4:7], 0 offen lds"]) == \
         ["M0 written right before an LDS copy"]
+    # a label between them does not separate them (a branch instruction does)
+    assert _rules(["s_cbranch_scc1 .LBB0_3", "s_mov_b32 m0, s3", ".LBB0_3:",
+                   "buffer_load_dwordx4 v1, s[4:7], 0 offen lds", "s_endpgm"]) == \
+        ["M0 written right before an LDS copy"]
+    assert _rules(["s_mov_b32 m0, s3", "s_branch .LBB0_3", ".LBB0_3:",
+                   "buffer_load_dwordx4 v1, s[4:7], 0 offen lds", "s_endpgm"]) == []
     st = ["global_store_dwordx4 v[8:9], v[4:7], off nt sc1", "s_or_b64 exec, exec, s[0:1]",
           "v_or_b32_e32 v4, 16, v134"]
-    assert [h[0] for h in hazards(st)] == ["store data overwritten within two instructions"]
-    assert hazards(st[:1] + ["s_nop 1"] + st[1:]) == []
+    assert _rules(st) == ["store data overwritten within two instructions"]
+    assert _rules(st[:1] + ["s_nop 1"] + st[1:]) == []
+    st_br = ["global_store_dwordx4 v[8:9], v[4:7], off nt sc1", "s_cbranch_scc1 .LBB0_4", "s_endpgm",
+             ".LBB0_4:", "v_or_b32_e32 v4, 16, v134", "s_endpgm"]
+    assert _rules(st_br) == ["store data overwritten within two instructions"]
     ld = ["global_store_dword v[2:3], v1, off nt sc1", "global_load_dword v5, v[6:7], off", "s_endpgm"]
-    assert [h[0] for h in hazards(ld)] == ["load after a write-through store"]
-    assert hazards(ld[:1] + ["s_endpgm"] + ld[1:]) == []
+    assert _rules(ld) == ["register load after a write-through store"]
+    assert _rules(ld[:1] + ["s_endpgm"] + ld[1:]) == []
+    # an LDS copy after the store, waited for with vmcnt(0): allowed; with a count: not
+    cp = ["global_store_dword v[2:3], v1, off nt sc1", "s_mov_b32 m0, s3", "s_nop 0",
+          "buffer_load_dwordx4 v1, s[4:7], 0 offen lds", "s_waitcnt vmcnt(0)", "s_endpgm"]
+    assert _rules(cp) == []
+    assert _rules(cp[:4] + ["s_waitcnt vmcnt(1) lgkmcnt(0)", "s_endpgm"]) == \
+        ["counted vector memory wait after a write-through store"]
+    # a store inside a loop reaches the loop head again
+    back = [".LBB0_5:", "s_waitcnt vmcnt(2)", "global_store_dword v[2:3], v1, off nt sc1",
+            "s_cbranch_scc1 .LBB0_5", "s_endpgm"]
+    assert _rules(back) == ["counted vector memory wait after a write-through store"]
 
 
 @pytest.mark.skipif(shutil.which(hip_build.hipcc()) is None and not os.path.exists(hip_build.hipcc()),
@@ -139,8 +236,8 @@ def test_library_kernels_have_no_hidden_hazards(tmp_path):
         results = list(ex.map(to_asm, srcs))
     problems, n_buffer = [], 0
     for src, text in results:
-        instrs = _instructions(text)
+        instrs, _ = _program(text.splitlines())
         n_buffer += sum(1 for x in instrs if x.startswith("buffer_"))
-        problems += [f"{os.path.basename(src)}: {rule}: {ins}" for rule, _, ins in hazards(instrs)]
+        problems += [f"{os.path.basename(src)}: {rule}: {ins}" for rule, _, ins in hazards(text.splitlines())]
     assert n_buffer > 100, "no buffer instructions found: the assembly was not parsed"
     assert not problems, "\n".join(problems[:20])
