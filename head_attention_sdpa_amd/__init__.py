@@ -165,6 +165,20 @@ def _lens_ptr(lens, batch, device):
     return lens.data_ptr()
 
 
+def _expect(t, shape, dtype, device, what):
+    """t must have exactly this shape, dtype and device (checked before any
+    pointer reaches the library: a smaller or mistyped tensor would be
+    written or read past its end)."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device:
+        raise ValueError(f"{what} must be {dtype} {tuple(shape)} on {device}; got {t.dtype} "
+                         f"{tuple(t.shape)} on {t.device}")
+
+
+def _on_gpu(t):
+    if t.device.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+
+
 def _stream(stream):
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
@@ -183,8 +197,9 @@ def sdpa(q, k, v, scale=None, causal=False, seqlens_q=None, seqlens_kv=None, ret
         raise ValueError("shape mismatch between q, k, v")
     if not (q.dtype == k.dtype == v.dtype) or not (q.device == k.device == v.device):
         raise ValueError("q, k, v must share dtype and device")
-    if q.device.type != "cuda":
-        raise ValueError("tensors must be on the GPU")
+    if out is not None:
+        _expect(out, (B, H, n_q, d_v), q.dtype, q.device, "out")
+    _on_gpu(q)
     dt = _dtype_code(q)
     if out is None:
         out = torch.empty((B, H, n_q, d_v), dtype=q.dtype, device=q.device)
@@ -208,6 +223,32 @@ def mha_workspace_bytes(batch, n_q, n_kv, d_model, heads, d_k=64, d_v=64, dtype=
     return int(lib().attn_mha_workspace_bytes(dtype, batch, n_q, n_kv, d_model, heads, d_k, d_v))
 
 
+def _check_projections(x_q, x_kv, w_q, w_k, w_v, w_o, heads, out, fn):
+    """Shapes of the multi-head block's operands: x_kv [B, n_kv, d_model],
+    w_q/w_k/w_v [d_model, heads*d_k], w_o [heads*d_v, d_model] with
+    heads*d_k = heads*d_v = d_model (d_k = d_v = d_model/h, "Attention Is All
+    You Need" section 3.2.2), out [B, n_q, d_model]; all contiguous, one
+    dtype and device.  Returns (d_k, d_v)."""
+    if x_q.dim() != 3 or x_kv.dim() != 3:
+        raise ValueError(f"{fn}: x_q and x_kv must be [batch, n, d_model]")
+    B, n_q, d_model = x_q.shape
+    if heads < 1 or d_model % heads != 0:
+        raise ValueError(f"{fn}: d_model = {d_model} is not a multiple of heads = {heads}")
+    d_k = d_v = d_model // heads
+    hd = heads * d_k
+    want = {"x_kv": (x_kv, (B, x_kv.shape[1], d_model)), "w_q": (w_q, (d_model, hd)),
+            "w_k": (w_k, (d_model, hd)), "w_v": (w_v, (d_model, hd)), "w_o": (w_o, (hd, d_model))}
+    if out is not None:
+        want["out"] = (out, (B, n_q, d_model))
+    for name, (t, shape) in want.items():
+        _expect(t, shape, x_q.dtype, x_q.device, f"{fn}: {name}")
+        if not t.is_contiguous():
+            raise ValueError(f"{fn}: {name} must be contiguous")
+    if not x_q.is_contiguous():
+        raise ValueError(f"{fn}: x_q must be contiguous")
+    return d_k, d_v
+
+
 def mha(x_q, x_kv, w_q, w_k, w_v, w_o, heads, scale=None, causal=False, seqlens_q=None,
         seqlens_kv=None, out=None, workspace=None, stream=None):
     """Multi-head attention block forward on the GPU (bf16, d_k = d_v = 64).
@@ -217,11 +258,8 @@ def mha(x_q, x_kv, w_q, w_k, w_v, w_o, heads, scale=None, causal=False, seqlens_
     torch = _torch()
     B, n_q, d_model = x_q.shape
     n_kv = x_kv.shape[1]
-    d_k = w_q.shape[1] // heads
-    d_v = w_v.shape[1] // heads
-    for t in (x_q, x_kv, w_q, w_k, w_v, w_o):
-        if not t.is_contiguous() or t.device != x_q.device or t.dtype != x_q.dtype:
-            raise ValueError("mha inputs must be contiguous and share device and dtype")
+    d_k, d_v = _check_projections(x_q, x_kv, w_q, w_k, w_v, w_o, heads, out, "mha")
+    _on_gpu(x_q)
     dt = _dtype_code(x_q)
     nbytes = mha_workspace_bytes(B, n_q, n_kv, d_model, heads, d_k, d_v, dt)
     if nbytes == 0:
@@ -259,20 +297,20 @@ def mha_block(x_q, w_q, w_k, w_v, w_o, ln_gamma, ln_beta, heads, x_kv=None, add_
     B, n_q, d_model = x_q.shape
     xkv = x_q if x_kv is None else x_kv
     n_kv = xkv.shape[1]
-    for t in (x_q, xkv, w_q, w_k, w_v, w_o, ln_gamma, ln_beta):
-        if not t.is_contiguous() or t.device != x_q.device or t.dtype != x_q.dtype:
-            raise ValueError("mha_block inputs must be contiguous and share device and dtype")
+    d_k, d_v = _check_projections(x_q, xkv, w_q, w_k, w_v, w_o, heads, out, "mha_block")
+    for name, t in (("ln_gamma", ln_gamma), ("ln_beta", ln_beta)):
+        _expect(t, (d_model,), x_q.dtype, x_q.device, f"mha_block: {name}")
+    _on_gpu(x_q)
     dt = _dtype_code(x_q)
-    nbytes = mha_block_workspace_bytes(B, n_q, n_kv, d_model, heads, add_pe, w_q.shape[1] // heads,
-                                       w_v.shape[1] // heads, dt)
+    nbytes = mha_block_workspace_bytes(B, n_q, n_kv, d_model, heads, add_pe, d_k, d_v, dt)
     if nbytes == 0:
         raise AttnError("attn_mha_block_workspace_bytes", -2, "unsupported sizes")
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=x_q.device)
     if out is None:
         out = torch.empty((B, n_q, d_model), dtype=x_q.dtype, device=x_q.device)
-    rc = lib().attn_mha_block_fwd(dt, B, n_q, n_kv, d_model, heads, w_q.shape[1] // heads,
-                                  w_v.shape[1] // heads, x_q.data_ptr(), xkv.data_ptr() or None,
+    rc = lib().attn_mha_block_fwd(dt, B, n_q, n_kv, d_model, heads, d_k, d_v,
+                                  x_q.data_ptr(), xkv.data_ptr() or None,
                                   int(bool(add_pe)), w_q.data_ptr(), w_k.data_ptr(), w_v.data_ptr(),
                                   w_o.data_ptr(), ln_gamma.data_ptr(), ln_beta.data_ptr(), float(ln_eps),
                                   out.data_ptr(), 0.0 if scale is None else float(scale),
@@ -298,6 +336,13 @@ def decode(q, k_cache, v_cache, scale=None, seqlens_kv=None, return_lse=False, o
     torch = _torch()
     B, H, n_q, d_k = q.shape
     n_kv, d_v = k_cache.shape[2], v_cache.shape[3]
+    _expect(k_cache, (B, H, n_kv, d_k), q.dtype, q.device, "decode: k_cache")
+    _expect(v_cache, (B, H, n_kv, d_v), q.dtype, q.device, "decode: v_cache")
+    if out is not None:
+        _expect(out, (B, H, n_q, d_v), q.dtype, q.device, "decode: out")
+    if workspace is not None and workspace.device != q.device:
+        raise ValueError("decode: workspace must be on the device of q")
+    _on_gpu(q)
     dt = _dtype_code(q)
     if out is None:
         out = torch.empty((B, H, n_q, d_v), dtype=q.dtype, device=q.device)
@@ -361,8 +406,12 @@ def sdpa_bwd(q, k, v, o, lse, dout, scale=None, causal=False, seqlens_q=None, se
     for t in (k, v, o, dout, lse):
         if t.device != q.device:
             raise ValueError("all tensors must be on the same device")
-    if q.device.type != "cuda":
-        raise ValueError("tensors must be on the GPU")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype):
+        raise ValueError("q, k, v, o and dout must share one dtype")
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t is not None:
+            _expect(t, like.shape, like.dtype, like.device, f"sdpa_bwd: {name}")
+    _on_gpu(q)
     dt = _dtype_code(q)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk

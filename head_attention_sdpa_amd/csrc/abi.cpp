@@ -176,20 +176,38 @@ struct MhaLayout {
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Sizes of the multi-head block.  The heads split the model width:
+// d_k = d_v = d_model / h ("Attention Is All You Need" section 3.2.2; the
+// rockcohen.cc deep read, section 5.2), so h*d_k != d_model or h*d_v !=
+// d_model is an invalid call, not an unsupported one.
 bool mha_sizes_ok(attn_dtype dt, int batch, int n_q, int n_kv, int d_model, int heads, int d_k,
                   int d_v, int* err) {
   if (dt != ATTN_F32 && dt != ATTN_BF16) { *err = ATTN_E_INVALID; return false; }
-  if (batch < 1 || n_q < 0 || n_kv < 0 || d_model < 1 || heads < 1 || d_k < 1 || d_v < 1) {
+  if (batch < 1 || n_q < 0 || n_kv < 0 || d_model < 1 || heads < 1 || d_k < 1 || d_v < 1 ||
+      (int64_t)heads * d_k != d_model || (int64_t)heads * d_v != d_model) {
     *err = ATTN_E_INVALID;
     return false;
   }
-  if (dt != ATTN_BF16 || d_k != 64 || d_v != 64 || d_model % 64 != 0) {
+  if (dt != ATTN_BF16 || d_k != 64 || d_v != 64) {
     *err = ATTN_E_UNSUPPORTED;
     return false;
   }
   // GEMM row counts and workspace offsets must fit the kernels' index types
   if ((int64_t)batch * n_q > kMaxGrid || (int64_t)batch * n_kv > kMaxGrid ||
       (int64_t)heads * 64 * 3 > kMaxGrid) {
+    *err = ATTN_E_UNSUPPORTED;
+    return false;
+  }
+  // The attention step reads the projections through 32-bit buffer offsets
+  // within each (b, h) slice, as attn_sdpa_fwd does: the rows a launch may
+  // touch (queries rounded up to 128, keys to 64) times the row stride of
+  // the workspace layout (3*h*64 elements for self-attention's fused
+  // [Q | K | V]; h*64 and 2*h*64 for cross-attention, bounded by the
+  // former) must stay below 2 GiB, and the grid must fit.
+  const int64_t row_bytes = 3LL * heads * 64 * 2;
+  const int64_t qrows = ((int64_t)n_q + 127) / 128 * 128, krows = ((int64_t)n_kv + 63) / 64 * 64;
+  if (qrows * row_bytes + 128 > 0x7fffffffLL || krows * row_bytes + 128 > 0x7fffffffLL ||
+      ((int64_t)n_q + 127) / 128 * batch * heads > kMaxGrid) {
     *err = ATTN_E_UNSUPPORTED;
     return false;
   }
@@ -348,6 +366,10 @@ int attn_sdpa_window_fwd(attn_dtype dt, int batch, int heads, int n_q, int n_kv,
   const int rc = check_sdpa(dt, batch, heads, n_q, n_kv, d_k, d_v, q, sq, k, sk, v, sv, o, so,
                             &scale, mask, lse, st);
   if (rc != ATTN_OK) return rc;
+  // |i - j| <= max(n_q, n_kv) holds for every pair, so a wider radius is the
+  // same call; clamping keeps the kernels' bound arithmetic (q0 + rows +
+  // window) in int range
+  if (window > n_q && window > n_kv) window = n_q > n_kv ? n_q : n_kv;
   return launch_sdpa(dt, batch, heads, n_q, n_kv, d_k, d_v, q, k, v, o, st, scale, mask, window,
                      seqlens_q, seqlens_kv, lse, static_cast<hipStream_t>(stream));
 }

@@ -108,8 +108,14 @@ def mha_call(dt=1, B=1, nq=16, nkv=16, dm=128, H=2, dk=64, dv=64, ws=FAKE, wsb=1
     (dict(scale=-2.0), -1),
     (dict(mask=9), -1),
     (dict(dt=0), -2),
-    (dict(dk=32), -2),
-    (dict(dm=100), -2),
+    # the heads split the model width: h * d_k = h * d_v = d_model
+    (dict(dk=32), -1),
+    (dict(dm=100), -1),
+    (dict(dm=128, H=4), -1),
+    (dict(dm=128, H=4, dk=32), -1),
+    (dict(dm=128, H=4, dk=32, dv=32), -2),   # a consistent split, but head size 32 is not built
+    # the attention step's 32-bit offsets: 87,297 rows of a 64-head fused QKV projection pass 2 GiB
+    (dict(nq=87297, nkv=87297, dm=4096, H=64), -2),
     (dict(ws=None), -4),
     (dict(wsb=1024), -4),
     (dict(ws=FAKE + 16), -3),
@@ -127,6 +133,14 @@ def test_mha_workspace_bytes():
     assert L.attn_mha_workspace_bytes(0, 4, 4096, 4096, 1024, 16, 64, 64) == 0  # f32 unsupported
     assert L.attn_mha_workspace_bytes(1, 4, 4096, 4096, 1000, 16, 64, 64) == 0
     assert L.attn_mha_workspace_bytes(1, 0, 4096, 4096, 1024, 16, 64, 64) == 0
+    assert L.attn_mha_workspace_bytes(1, 4, 4096, 4096, 1024, 8, 64, 64) == 0   # 8 * 64 != 1024
+    assert L.attn_mha_workspace_bytes(1, 4, 4096, 4096, 1024, 16, 64, 32) == 0  # 16 * 32 != 1024
+    # rows x 3*64*64*2 bytes per fused projection row: 87,296 rows fit below 2 GiB, 87,297 do not
+    assert L.attn_mha_workspace_bytes(1, 1, 87296, 87296, 4096, 64, 64, 64) > 0
+    assert L.attn_mha_workspace_bytes(1, 1, 87297, 87297, 4096, 64, 64, 64) == 0
+    # keys round up to 64 rows: 87,360 fit, 87,361 do not
+    assert L.attn_mha_workspace_bytes(1, 1, 16, 87360, 4096, 64, 64, 64) > 0
+    assert L.attn_mha_workspace_bytes(1, 1, 16, 87361, 4096, 64, 64, 64) == 0
 
 
 def linear_call(dt=1, m=64, k=128, n=256, x=FAKE, ldx=128, w=FAKE, y=FAKE, ldy=256):
@@ -269,9 +283,11 @@ def block_call(dt=1, B=2, nq=64, nkv=64, dm=256, H=4, dk=64, dv=64, xq=FAKE, xkv
     (dict(eps=float("inf")), -1),
     (dict(scale=-1.0), -1),
     (dict(dt=0), -2),
-    (dict(dm=320), -2),                      # d_model outside {256, 512, 768, 1024}
+    (dict(dm=320, H=5), -2),                 # d_model outside {256, 512, 768, 1024}
+    (dict(dm=320), -1),                      # 4 heads of 64 are not 320 wide
     (dict(dm=2048, H=32), -2),
-    (dict(dk=32, dv=32), -2),
+    (dict(dk=32, dv=32), -1),                # 4 heads of 32 are not 256 wide
+    (dict(dk=32, dv=32, H=8), -2),           # 8 heads of 32 are, but head size 32 is not built
     (dict(g=MISALIGNED), -3),
     (dict(ws=FAKE + 64), -3),
     (dict(ws=None), -4),
@@ -289,3 +305,91 @@ def test_mha_block_workspace_bytes():
     assert L.attn_mha_block_workspace_bytes(1, 4, 4096, 4096, 1024, 16, 64, 64, 0) == base
     assert L.attn_mha_block_workspace_bytes(1, 4, 4096, 4096, 1024, 16, 64, 64, 1) == base + 4 * 4096 * 1024 * 2
     assert L.attn_mha_block_workspace_bytes(1, 4, 4096, 4096, 320, 5, 64, 64, 0) == 0
+
+
+# ---------------------------------------------------------------------------
+# The binding checks every tensor whose pointer it passes against the shape,
+# dtype and device the call implies, before anything reaches the library (a
+# smaller or mistyped out, cache or weight would be written or read past its
+# end).  The shape checks come first, so CPU tensors exercise them here.
+# ---------------------------------------------------------------------------
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def test_binding_sdpa_checks_out():
+    q = _t(2, 3, 10, 64)
+    with pytest.raises(ValueError, match="out must be"):
+        attn.sdpa(q, q, q, out=_t(2, 3, 9, 64))
+    import torch
+    with pytest.raises(ValueError, match="out must be"):
+        attn.sdpa(q, q, q, out=_t(2, 3, 10, 64, dtype=torch.float32))
+    with pytest.raises(ValueError, match="on the GPU"):
+        attn.sdpa(q, q, q, out=_t(2, 3, 10, 64))
+
+
+def test_binding_decode_checks_caches_and_out():
+    q = _t(2, 3, 1, 64)
+    cache = _t(2, 3, 100, 64)
+    with pytest.raises(ValueError, match="k_cache"):
+        attn.decode(q, _t(2, 4, 100, 64), cache)
+    with pytest.raises(ValueError, match="k_cache"):
+        attn.decode(q, _t(1, 3, 100, 64), cache)
+    with pytest.raises(ValueError, match="v_cache"):
+        attn.decode(q, cache, _t(2, 3, 99, 64))
+    with pytest.raises(ValueError, match="out"):
+        attn.decode(q, cache, cache, out=_t(2, 3, 2, 64))
+    with pytest.raises(ValueError, match="on the GPU"):
+        attn.decode(q, cache, cache)
+
+
+def _mha_operands(B=2, n_q=8, n_kv=6, dm=128, heads=2):
+    x, xkv = _t(B, n_q, dm), _t(B, n_kv, dm)
+    w = [_t(dm, dm) for _ in range(4)]
+    return x, xkv, w, heads
+
+
+@pytest.mark.parametrize("bad,match", [
+    ("w_q", "w_q"), ("w_k", "w_k"), ("w_v", "w_v"), ("w_o", "w_o"), ("x_kv", "x_kv"), ("out", "out"),
+    ("heads", "multiple of heads"),
+])
+def test_binding_mha_checks_operands(bad, match):
+    x, xkv, w, heads = _mha_operands()
+    kw = {}
+    if bad == "x_kv":
+        xkv = _t(2, 6, 64)
+    elif bad == "out":
+        kw["out"] = _t(2, 8, 64)
+    elif bad == "heads":
+        heads = 3
+    else:
+        w[("w_q", "w_k", "w_v", "w_o").index(bad)] = _t(128, 64)
+    with pytest.raises(ValueError, match=match):
+        attn.mha(x, xkv, *w, heads=heads, **kw)
+    x, xkv, w, heads = _mha_operands(dm=256, heads=4)
+    g = _t(256)
+    if bad in ("w_q", "w_k", "w_v", "w_o"):
+        w[("w_q", "w_k", "w_v", "w_o").index(bad)] = _t(256, 128)
+        with pytest.raises(ValueError, match=match):
+            attn.mha_block(x, *w, g, g, heads=4, x_kv=xkv)
+    with pytest.raises(ValueError, match="ln_gamma"):
+        attn.mha_block(x, *_mha_operands(dm=256, heads=4)[2], _t(128), g, heads=4)
+
+
+def test_binding_mha_reaches_gpu_check_when_consistent():
+    x, xkv, w, heads = _mha_operands()
+    with pytest.raises(ValueError, match="on the GPU"):
+        attn.mha(x, xkv, *w, heads=heads)
+
+
+def test_binding_bwd_checks_gradients():
+    q = _t(1, 2, 10, 64)
+    k = _t(1, 2, 12, 64)
+    import torch
+    lse = torch.zeros((1, 2, 10), dtype=torch.float32)
+    for name, bad in (("dq", _t(1, 2, 12, 64)), ("dk", _t(1, 2, 10, 64)), ("dv", _t(1, 2, 12, 32))):
+        with pytest.raises(ValueError, match=name):
+            attn.sdpa_bwd(q, k, k, q, lse, q, **{name: bad})
+    with pytest.raises(ValueError, match="on the GPU"):
+        attn.sdpa_bwd(q, k, k, q, lse, q)

@@ -81,12 +81,12 @@ def run(name, B, n_q, n_kv, dm, heads, causal, add_pe, cross=False, lq=None, lkv
 
 CASES = [
     dict(name="self_causal_pe_ragged", B=2, n_q=300, n_kv=300, dm=256, heads=4, causal=True, add_pe=True),
-    dict(name="self_bidir_pe_lengths", B=2, n_q=200, n_kv=200, dm=512, heads=4, causal=False, add_pe=True,
+    dict(name="self_bidir_pe_lengths", B=2, n_q=200, n_kv=200, dm=512, heads=8, causal=False, add_pe=True,
          lq=[200, 77], lkv=[200, 77]),
     dict(name="cross_key_lengths", B=2, n_q=150, n_kv=97, dm=768, heads=12, causal=False, add_pe=False,
          cross=True, lkv=[97, 40]),
     dict(name="self_no_pe_d1024", B=1, n_q=130, n_kv=130, dm=1024, heads=16, causal=True, add_pe=False),
-    dict(name="one_row_tile_tail", B=3, n_q=21, n_kv=21, dm=256, heads=2, causal=False, add_pe=True),
+    dict(name="one_row_tile_tail", B=3, n_q=21, n_kv=21, dm=256, heads=4, causal=False, add_pe=True),
     dict(name="cross_empty_memory", B=2, n_q=70, n_kv=0, dm=256, heads=4, causal=False, add_pe=False,
          cross=True),
     dict(name="cross_causal_nq_gt_nkv", B=1, n_q=200, n_kv=90, dm=512, heads=8, causal=True, add_pe=False,

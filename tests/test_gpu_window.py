@@ -78,3 +78,21 @@ def test_window_f32_vs_oracle(r, causal):
 def test_window_long_sequence():
     """The block's sequence length with a 256-key radius: 16 heads x 4096."""
     run_case("long_r256", "bf16", 1, 16, 4096, 4096, 256, True, seed=5)
+
+
+@pytest.mark.parametrize("dtype,causal", [("bf16", True), ("bf16", False), ("f32", True)])
+def test_window_int_max_is_full_attention(dtype, causal):
+    """A radius beyond every |i - j| leaves every key legal: r = 2^31 - 1
+    (which the library clamps before its bound arithmetic) gives bitwise the
+    same output as the radius max(n_q, n_kv), and unrestricted attention
+    within tolerance of the oracle."""
+    import torch
+    attn = attn_mod()
+    d = 64 if dtype == "bf16" else 16
+    og, inp = run_case(f"int_max_{dtype}_{causal}", dtype, 2, 2, 333, 333, 2 ** 31 - 1, causal, seed=6, d=d)
+    q, k, v = (to_gpu(a, dtype) for a in (inp.q_st, inp.k_st, inp.v_st))
+    o2 = attn.sdpa(q, k, v, scale=0.125, causal=causal, window=333)
+    torch.cuda.synchronize()
+    assert np.array_equal(og, to_f64(o2))
+    ref, _ = oracle.sdpa(inp.q, inp.k, inp.v, scale=0.125, causal=causal)
+    assert max_err(og, ref) <= (2e-2 if dtype == "bf16" else 1e-4)

@@ -646,3 +646,66 @@ def test_block_cross_and_rows():
     ys, _ = oracle.mha_block(x, wq, wk, wv, wo, g, b, heads=2, add_pe=True, causal=True)
     ysr, _ = oracle.mha_block_rows(x, wq, wk, wv, wo, g, b, heads=2, rows=rows, add_pe=True, causal=True)
     assert np.array_equal(ysr, ys.reshape(-1, 8)[rows])
+
+
+# ---------------------------------------------------------------------------
+# Brute force at 50 digits on tiny shapes: Eq. 1 evaluated literally (no max
+# shift, no reordering) in mpmath, against the oracle's fp64 stable form.
+# ---------------------------------------------------------------------------
+def _mp_sdpa_row(mp, q, K, V, scale, legal):
+    s = [scale * mp.fsum(mp.mpf(a) * mp.mpf(b) for a, b in zip(q, K[j])) for j in legal]
+    e = [mp.exp(x) for x in s]
+    z = mp.fsum(e)
+    o = [mp.fsum(e[t] * mp.mpf(V[j][c]) for t, j in enumerate(legal)) / z for c in range(len(V[0]))]
+    return o, mp.log(z)
+
+
+@pytest.mark.parametrize("n_q,n_kv,d,causal,lkv", [(2, 2, 2, False, None), (3, 4, 5, True, None),
+                                                    (4, 3, 3, False, [2]), (4, 4, 4, True, [3])])
+def test_sdpa_matches_50_digit_brute_force(n_q, n_kv, d, causal, lkv):
+    """The oracle's fp64 result (max shift, fixed summation order) equals the
+    definition evaluated at 50 significant digits to 1e-13.  Catches any
+    cancellation or shift mistake that the closed forms above would not see
+    at these sizes."""
+    mp = pytest.importorskip("mpmath")
+    mp.mp.dps = 50
+    q, k, v = rnd(8101, (1, 1, n_q, d)) * 3, rnd(8102, (1, 1, n_kv, d)) * 3, rnd(8103, (1, 1, n_kv, d))
+    scale = 1 / math.sqrt(d)
+    lk = None if lkv is None else np.array(lkv, np.int32)
+    o, lse = oracle.sdpa(q, k, v, scale=scale, causal=causal, seqlens_kv=lk)
+    L = n_kv if lkv is None else lkv[0]
+    for i in range(n_q):
+        legal = [j for j in range(L) if not (causal and j > i)]
+        if not legal:
+            assert np.all(o[0, 0, i] == 0.0) and lse[0, 0, i] == -np.inf
+            continue
+        o_mp, lse_mp = _mp_sdpa_row(mp, q[0, 0, i], k[0, 0], v[0, 0], mp.mpf(scale), legal)
+        assert max(abs(float(o_mp[c]) - o[0, 0, i, c]) for c in range(d)) <= 1e-13
+        assert abs(float(lse_mp) - lse[0, 0, i]) <= 1e-13
+
+
+def test_mha_matches_50_digit_brute_force():
+    """MultiHead(X, X, X) = Concat(head_1, head_2) W^O with head_i =
+    Attention(X W^Q_i, X W^K_i, X W^V_i) (section 3.2.2), two heads of size
+    2, evaluated at 50 digits: equals the oracle to 1e-13."""
+    mp = pytest.importorskip("mpmath")
+    mp.mp.dps = 50
+    n, dm, h = 3, 4, 2
+    x = rnd(8111, (1, n, dm))
+    w = [rnd(8112 + t, (dm, dm)) * 0.5 for t in range(4)]
+    y = oracle.mha(x, x, *w, heads=h, causal=True)
+    X = mp.matrix(x[0].tolist())
+    Wq, Wk, Wv, Wo = (mp.matrix(m.tolist()) for m in w)
+    Qp, Kp, Vp = X * Wq, X * Wk, X * Wv
+    dk = dm // h
+    cat = mp.matrix(n, dm)
+    for hh in range(h):
+        cols = range(hh * dk, (hh + 1) * dk)
+        for i in range(n):
+            row, _ = _mp_sdpa_row(mp, [Qp[i, c] for c in cols], [[Kp[j, c] for c in cols] for j in range(n)],
+                                  [[Vp[j, c] for c in cols] for j in range(n)], 1 / mp.sqrt(dk),
+                                  list(range(i + 1)))
+            for t, c in enumerate(cols):
+                cat[i, c] = row[t]
+    Y = cat * Wo
+    assert max(abs(float(Y[i, c]) - y[0, i, c]) for i in range(n) for c in range(dm)) <= 1e-13
