@@ -183,8 +183,10 @@ static void sdpa_range(void* p, int64_t begin, int64_t end, double* s) {
     }
     int legal_begin = 0;
     if (c->window >= 0) {                             /* restricted: the neighbourhood |i - j| <= r */
-      legal_begin = i - c->window;
-      if (i + c->window + 1 < legal_end) legal_end = i + c->window + 1;
+      /* in 64 bits: i + r + 1 exceeds int range for a radius near INT_MAX */
+      const long long lo = (long long)i - c->window, hi = (long long)i + c->window + 1;
+      legal_begin = lo < 0 ? 0 : (int)lo;
+      if (hi < legal_end) legal_end = (int)hi;
     }
     sdpa_row(q, K, c->d_k, V, c->d_v, c->n_kv, c->d_k, c->d_v, c->scale, legal_begin, legal_end,
              causal_i, s, out, lse);

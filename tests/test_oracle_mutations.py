@@ -33,9 +33,8 @@ MUTATIONS = {
                           "const double* vj = V + (int64_t)(j == 0 ? 0 : j - 1) * v_stride;"),
     "decode alignment off by one": ("int pos = legal_end - c->n_q + i;", "int pos = legal_end - c->n_q + i + 1;"),
     "decode aligned at the start": ("int pos = legal_end - c->n_q + i;", "int pos = i;"),
-    "window one short on the left": ("legal_begin = i - c->window;", "legal_begin = i - c->window + 1;"),
-    "window one long on the right": ("if (i + c->window + 1 < legal_end) legal_end = i + c->window + 1;",
-                                     "if (i + c->window + 2 < legal_end) legal_end = i + c->window + 2;"),
+    "window one short on the left": ("lo = (long long)i - c->window,", "lo = (long long)i - c->window + 1,"),
+    "window one long on the right": ("hi = (long long)i + c->window + 1;", "hi = (long long)i + c->window + 2;"),
     "bwd softmax Jacobian without D": ("double ds = P[j] * (dp - D);", "double ds = P[j] * dp;"),
     "bwd dK without scale": ("for (int x = 0; x < c->d_k; ++x) dkj[x] += c->scale * ds * qi[x];",
                              "for (int x = 0; x < c->d_k; ++x) dkj[x] += ds * qi[x];"),

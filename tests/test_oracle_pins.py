@@ -431,6 +431,9 @@ def test_window_wider_than_the_sequence_is_full_attention():
         full = oracle.sdpa(q, k, v, causal=causal)
         win = oracle.sdpa(q, k, v, causal=causal, window=18)
         assert np.array_equal(full[0], win[0]) and np.array_equal(full[1], win[1])
+        # the largest radius the call takes: no overflow in the bounds, every key in the window
+        wmax = oracle.sdpa(q, k, v, causal=causal, window=2 ** 31 - 1)
+        assert np.array_equal(full[0], wmax[0]) and np.array_equal(full[1], wmax[1])
 
 
 def test_window_zero_attends_to_itself():
