@@ -74,27 +74,21 @@ def test_mha_block_vs_oracle(case):
             assert np.all(y[b, lq[b]:] == 0.0)
 
 
-def test_mha_full_size_workload_sampled_rows():
+def test_mha_full_size_workload_every_element():
     """The full multi-head block workload: X [4,4096,1024] = N(0,1) + PE,
-    Xavier W, h = 16, causal.  The oracle computes sampled output rows (all of
-    K/V for the sampled batch elements)."""
+    Xavier W, h = 16, causal, in the launch configuration the benchmark
+    times.  Every one of the 4 x 4096 x 1024 outputs is compared with the
+    fp64 oracle's (which runs the whole block, "Attention Is All You Need"
+    section 3.2.2) at the bf16 contract 2e-2."""
     inp = gen.config(5)
-    announce(f"mha full-size {inp.name}")
+    announce(f"mha full-size {inp.name}, every element")
     y = run_block(inp.x, inp.x, [inp.w_q, inp.w_k, inp.w_v, inp.w_o], inp.heads, True,
                   self_attn=True)
-    rng = np.random.default_rng(11)
-    rows = []
-    for b in (0, 3):
-        for i in sorted(set([0, 1, 63, 64, 127, 128, 2047, 4095] + list(rng.integers(0, 4096, 8)))):
-            rows.append(b * 4096 + i)
-    rows = np.array(rows)
-    y_ref = oracle.mha_rows(inp.x, inp.x, inp.w_q, inp.w_k, inp.w_v, inp.w_o, heads=16,
-                            rows=rows, causal=True)
-    y_s = y.reshape(-1, 1024)[rows]
-    err = max_err(y_s, y_ref)
-    y_st = oracle.mha_rows(inp.x, inp.x, inp.w_q, inp.w_k, inp.w_v, inp.w_o, heads=16, rows=rows,
-                           causal=True, bf16_storage=True)
-    print(f"  full-size mha: max|gpu-oracle| = {err:.3e} over {len(rows)} rows; "
-          f"vs storage-rounded oracle {max_err(y_s, y_st):.3e}", flush=True)
     assert np.all(np.isfinite(y))
+    y_ref = oracle.mha(inp.x, inp.x, inp.w_q, inp.w_k, inp.w_v, inp.w_o, heads=16, causal=True)
+    d = np.abs(y - y_ref)
+    err = float(d.max())
+    print(f"  full-size mha: max|gpu-oracle| = {err:.3e} over {d.size} outputs "
+          f"(99.99th percentile {np.percentile(d, 99.99):.3e}, {int((d > 1e-2).sum())} above 1e-2; "
+          f"max|y| {np.abs(y_ref).max():.2f})", flush=True)
     assert err <= TOL
