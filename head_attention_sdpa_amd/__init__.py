@@ -30,7 +30,7 @@ STATUS = {0: "ATTN_OK", -1: "ATTN_E_INVALID", -2: "ATTN_E_UNSUPPORTED", -3: "ATT
 # every entry point that include/attn_sdpa.h declares
 EXPORTS = ("attn_sdpa_fwd", "attn_sdpa_window_fwd", "attn_mha_workspace_bytes", "attn_mha_fwd", "attn_decode_workspace_bytes",
            "attn_decode_fwd", "attn_linear_fwd", "attn_mha_block_workspace_bytes", "attn_mha_block_fwd",
-           "attn_sdpa_bwd_workspace_bytes", "attn_sdpa_bwd",
+           "attn_sdpa_bwd_workspace_bytes", "attn_sdpa_bwd", "attn_sdpa_bwd_noalloc",
            "attn_status_str", "attn_last_hip_error", "attn_hip_error_str", "attn_abi_version")
 
 
@@ -107,6 +107,9 @@ def lib() -> ctypes.CDLL:
                                     vp, sp, vp, sp, vp, sp, ctypes.c_float, i, vp, vp, vp,
                                     ctypes.c_size_t, vp]
         L.attn_sdpa_bwd.restype = i
+        L.attn_sdpa_bwd_noalloc.argtypes = [i, i, i, i, i, i, i, vp, sp, vp, sp, vp, sp, vp, sp, vp, sp, vp,
+                                            vp, sp, vp, sp, vp, sp, ctypes.c_float, i, vp, vp, vp]
+        L.attn_sdpa_bwd_noalloc.restype = i
         L.attn_status_str.argtypes = [i]
         L.attn_status_str.restype = ctypes.c_char_p
         L.attn_abi_version.argtypes = []
@@ -389,11 +392,14 @@ def sdpa_bwd_workspace_bytes(batch, heads, n_q, n_kv, d_k=64, d_v=64, dtype=ATTN
 
 
 def sdpa_bwd(q, k, v, o, lse, dout, scale=None, causal=False, seqlens_q=None, seqlens_kv=None,
-             dq=None, dk=None, dv=None, workspace=None, stream=None):
+             dq=None, dk=None, dv=None, workspace=None, stream=None, noalloc=False):
     """Gradients of scaled dot-product attention (bf16, head size 64): given
     the forward's q, k, v, its output o and lse [B,H,n_q] (fp32, contiguous)
     and the gradient dout of o, returns (dq, dk, dv).  scale, causal and the
-    lengths must be those of the forward call."""
+    lengths must be those of the forward call.  noalloc=True calls
+    attn_sdpa_bwd_noalloc (no workspace; the library's fixed per-device
+    scratch, B*H*n_q <= 2,097,152; pass dq, dk, dv to allocate nothing here
+    either)."""
     torch = _torch()
     B, H, n_q, d_k = q.shape
     n_kv, d_v = k.shape[2], v.shape[3]
@@ -416,11 +422,23 @@ def sdpa_bwd(q, k, v, o, lse, dout, scale=None, causal=False, seqlens_q=None, se
     dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
     dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
     dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    st = [_strides4(t) for t in (q, k, v, o, dout, dq, dk, dv)]
+    ptr = [t.data_ptr() or None for t in (q, k, v, o, dout, dq, dk, dv)]
+    if noalloc:
+        rc = lib().attn_sdpa_bwd_noalloc(dt, B, H, n_q, n_kv, d_k, d_v,
+                                         ptr[0], ctypes.byref(st[0]), ptr[1], ctypes.byref(st[1]),
+                                         ptr[2], ctypes.byref(st[2]), ptr[3], ctypes.byref(st[3]),
+                                         ptr[4], ctypes.byref(st[4]), lse.data_ptr() or None,
+                                         ptr[5], ctypes.byref(st[5]), ptr[6], ctypes.byref(st[6]),
+                                         ptr[7], ctypes.byref(st[7]), 0.0 if scale is None else float(scale),
+                                         ATTN_MASK_CAUSAL if causal else ATTN_MASK_NONE,
+                                         _lens_ptr(seqlens_q, B, q.device), _lens_ptr(seqlens_kv, B, q.device),
+                                         _stream(stream))
+        _check("attn_sdpa_bwd_noalloc", rc)
+        return dq, dk, dv
     nbytes = sdpa_bwd_workspace_bytes(B, H, n_q, n_kv, d_k, d_v, dt)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
-    st = [_strides4(t) for t in (q, k, v, o, dout, dq, dk, dv)]
-    ptr = [t.data_ptr() or None for t in (q, k, v, o, dout, dq, dk, dv)]
     rc = lib().attn_sdpa_bwd(dt, B, H, n_q, n_kv, d_k, d_v,
                              ptr[0], ctypes.byref(st[0]), ptr[1], ctypes.byref(st[1]),
                              ptr[2], ctypes.byref(st[2]), ptr[3], ctypes.byref(st[3]),

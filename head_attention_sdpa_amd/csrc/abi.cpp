@@ -320,6 +320,75 @@ bool block_dmodel_ok(int d_model) {
   return d_model == 256 || d_model == 512 || d_model == 768 || d_model == 1024;
 }
 
+// The backward's checks and launches; `workspace` is the caller's buffer or
+// the fixed scratch (scratch_call: already looked up and sized).
+int sdpa_bwd_impl(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k, int d_v,
+                  const void* q, const attn_strides* sq, const void* k, const attn_strides* sk,
+                  const void* v, const attn_strides* sv, const void* o, const attn_strides* so,
+                  const void* dout, const attn_strides* sdo, const float* lse, void* dq,
+                  const attn_strides* sdq, void* dk, const attn_strides* sdk, void* dv,
+                  const attn_strides* sdv, float scale, attn_mask mask, const int32_t* seqlens_q,
+                  const int32_t* seqlens_kv, bool scratch_call, void* workspace, size_t workspace_bytes,
+                  attn_stream_t stream) {
+  int err = ATTN_OK;
+  if (!bwd_sizes_ok(dt, batch, heads, n_q, n_kv, d_k, d_v, &err)) return err;
+  attn_strides st[4];
+  const int rc = check_sdpa(dt, batch, heads, n_q, n_kv, d_k, d_v, q, sq, k, sk, v, sv,
+                            const_cast<void*>(o), so, &scale, mask, lse, st);
+  if (rc != ATTN_OK) return rc;
+  // the gradients have the shapes of q, k and v; dO that of o
+  if ((n_q > 0 && (!dout || !dq || !lse)) || (n_kv > 0 && (!dk || !dv))) return ATTN_E_INVALID;
+  const attn_strides s_do = resolve(sdo, heads, n_q, 64), s_dq = resolve(sdq, heads, n_q, 64);
+  const attn_strides s_dk = resolve(sdk, heads, n_kv, 64), s_dv = resolve(sdv, heads, n_kv, 64);
+  const attn_strides* extra[4] = {&s_do, &s_dq, &s_dk, &s_dv};
+  for (const attn_strides* e : extra) {
+    if (!strides_ok(*e)) return ATTN_E_INVALID;
+    if (!strides_aligned(*e, 8)) return ATTN_E_ALIGN;
+  }
+  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return ATTN_E_ALIGN;
+  // dO rows stream through the same 32-bit buffer offsets as Q rows
+  if (n_q > 1 && s_do.n < 64) return ATTN_E_UNSUPPORTED;
+  if ((((int64_t)n_q + 127) / 128 * 128) * s_do.n * 2 + 128 > 0x7fffffffLL) return ATTN_E_UNSUPPORTED;
+  if (n_q > 0) {
+    if (scratch_call) {
+      // the fixed scratch: sizes beyond it are rejected before any HIP call
+      if (bwd_workspace(batch, heads, n_q) > attn::kBwdScratchBytes) return ATTN_E_WORKSPACE;
+      if (hip_status(attn::bwd_scratch(&workspace)) != ATTN_OK) return ATTN_E_HIP;
+      workspace_bytes = attn::kBwdScratchBytes;
+    }
+    if (!workspace || workspace_bytes < bwd_workspace(batch, heads, n_q)) return ATTN_E_WORKSPACE;
+    if (!aligned(workspace, 256)) return ATTN_E_ALIGN;
+  }
+  if (n_q == 0 && n_kv == 0) return ATTN_OK;   // nothing to do: no launch
+  SdpaBwdParams p = {};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(o);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.ld = static_cast<float*>(workspace);
+  p.seqlens_q = seqlens_q;
+  p.seqlens_kv = seqlens_kv;
+  p.qs_b = st[0].b; p.qs_h = st[0].h; p.qs_n = st[0].n;
+  p.ks_b = st[1].b; p.ks_h = st[1].h; p.ks_n = st[1].n;
+  p.vs_b = st[2].b; p.vs_h = st[2].h; p.vs_n = st[2].n;
+  p.os_b = st[3].b; p.os_h = st[3].h; p.os_n = st[3].n;
+  p.dos_b = s_do.b; p.dos_h = s_do.h; p.dos_n = s_do.n;
+  p.dqs_b = s_dq.b; p.dqs_h = s_dq.h; p.dqs_n = s_dq.n;
+  p.dks_b = s_dk.b; p.dks_h = s_dk.h; p.dks_n = s_dk.n;
+  p.dvs_b = s_dv.b; p.dvs_h = s_dv.h; p.dvs_n = s_dv.n;
+  p.batch = batch; p.heads = heads; p.n_q = n_q; p.n_kv = n_kv;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.causal = mask == ATTN_MASK_CAUSAL;
+  return hip_status(attn::launch_sdpa_bwd_bf16(p, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -561,57 +630,21 @@ int attn_sdpa_bwd(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_
                   const attn_strides* sdv, float scale, attn_mask mask, const int32_t* seqlens_q,
                   const int32_t* seqlens_kv, void* workspace, size_t workspace_bytes,
                   attn_stream_t stream) {
-  int err = ATTN_OK;
-  if (!bwd_sizes_ok(dt, batch, heads, n_q, n_kv, d_k, d_v, &err)) return err;
-  attn_strides st[4];
-  const int rc = check_sdpa(dt, batch, heads, n_q, n_kv, d_k, d_v, q, sq, k, sk, v, sv,
-                            const_cast<void*>(o), so, &scale, mask, lse, st);
-  if (rc != ATTN_OK) return rc;
-  // the gradients have the shapes of q, k and v; dO that of o
-  if ((n_q > 0 && (!dout || !dq || !lse)) || (n_kv > 0 && (!dk || !dv))) return ATTN_E_INVALID;
-  const attn_strides s_do = resolve(sdo, heads, n_q, 64), s_dq = resolve(sdq, heads, n_q, 64);
-  const attn_strides s_dk = resolve(sdk, heads, n_kv, 64), s_dv = resolve(sdv, heads, n_kv, 64);
-  const attn_strides* extra[4] = {&s_do, &s_dq, &s_dk, &s_dv};
-  for (const attn_strides* e : extra) {
-    if (!strides_ok(*e)) return ATTN_E_INVALID;
-    if (!strides_aligned(*e, 8)) return ATTN_E_ALIGN;
-  }
-  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
-    return ATTN_E_ALIGN;
-  // dO rows stream through the same 32-bit buffer offsets as Q rows
-  if (n_q > 1 && s_do.n < 64) return ATTN_E_UNSUPPORTED;
-  if ((((int64_t)n_q + 127) / 128 * 128) * s_do.n * 2 + 128 > 0x7fffffffLL) return ATTN_E_UNSUPPORTED;
-  if (n_q > 0) {
-    if (!workspace || workspace_bytes < bwd_workspace(batch, heads, n_q)) return ATTN_E_WORKSPACE;
-    if (!aligned(workspace, 256)) return ATTN_E_ALIGN;
-  }
-  if (n_q == 0 && n_kv == 0) return ATTN_OK;   // nothing to do: no launch
-  SdpaBwdParams p = {};
-  p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k);
-  p.v = static_cast<const uint16_t*>(v);
-  p.o = static_cast<const uint16_t*>(o);
-  p.dout = static_cast<const uint16_t*>(dout);
-  p.lse = lse;
-  p.dq = static_cast<uint16_t*>(dq);
-  p.dk = static_cast<uint16_t*>(dk);
-  p.dv = static_cast<uint16_t*>(dv);
-  p.ld = static_cast<float*>(workspace);
-  p.seqlens_q = seqlens_q;
-  p.seqlens_kv = seqlens_kv;
-  p.qs_b = st[0].b; p.qs_h = st[0].h; p.qs_n = st[0].n;
-  p.ks_b = st[1].b; p.ks_h = st[1].h; p.ks_n = st[1].n;
-  p.vs_b = st[2].b; p.vs_h = st[2].h; p.vs_n = st[2].n;
-  p.os_b = st[3].b; p.os_h = st[3].h; p.os_n = st[3].n;
-  p.dos_b = s_do.b; p.dos_h = s_do.h; p.dos_n = s_do.n;
-  p.dqs_b = s_dq.b; p.dqs_h = s_dq.h; p.dqs_n = s_dq.n;
-  p.dks_b = s_dk.b; p.dks_h = s_dk.h; p.dks_n = s_dk.n;
-  p.dvs_b = s_dv.b; p.dvs_h = s_dv.h; p.dvs_n = s_dv.n;
-  p.batch = batch; p.heads = heads; p.n_q = n_q; p.n_kv = n_kv;
-  p.scale = scale;
-  p.scale_log2 = scale * 1.4426950408889634f;
-  p.causal = mask == ATTN_MASK_CAUSAL;
-  return hip_status(attn::launch_sdpa_bwd_bf16(p, static_cast<hipStream_t>(stream)));
+  return sdpa_bwd_impl(dt, batch, heads, n_q, n_kv, d_k, d_v, q, sq, k, sk, v, sv, o, so, dout, sdo, lse,
+                       dq, sdq, dk, sdk, dv, sdv, scale, mask, seqlens_q, seqlens_kv, false, workspace,
+                       workspace_bytes, stream);
+}
+
+int attn_sdpa_bwd_noalloc(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k, int d_v,
+                          const void* q, const attn_strides* sq, const void* k, const attn_strides* sk,
+                          const void* v, const attn_strides* sv, const void* o, const attn_strides* so,
+                          const void* dout, const attn_strides* sdo, const float* lse, void* dq,
+                          const attn_strides* sdq, void* dk, const attn_strides* sdk, void* dv,
+                          const attn_strides* sdv, float scale, attn_mask mask, const int32_t* seqlens_q,
+                          const int32_t* seqlens_kv, attn_stream_t stream) {
+  return sdpa_bwd_impl(dt, batch, heads, n_q, n_kv, d_k, d_v, q, sq, k, sk, v, sv, o, so, dout, sdo, lse,
+                       dq, sdq, dk, sdk, dv, sdv, scale, mask, seqlens_q, seqlens_kv, true, nullptr, 0,
+                       stream);
 }
 
 }  // extern "C"

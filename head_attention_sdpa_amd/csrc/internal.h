@@ -151,6 +151,11 @@ hipError_t launch_sdpa_bf16(const SdpaBf16Params& p, hipStream_t stream);
 hipError_t launch_sdpa_f32(const SdpaF32Params& p, hipStream_t stream);
 hipError_t launch_sdpa_decode_bf16(const SdpaDecodeParams& p, hipStream_t stream);
 hipError_t launch_sdpa_bwd_bf16(const SdpaBwdParams& p, hipStream_t stream);
+// The backward's fixed per-device scratch (for callers that cannot allocate):
+// its size, and its device address on the current device (looked up once
+// per device).
+constexpr size_t kBwdScratchBytes = (size_t)16 << 20;
+hipError_t bwd_scratch(void** ptr);
 hipError_t launch_gemm_bf16(const GemmBf16Params& p, hipStream_t stream);
 hipError_t launch_pe_add_bf16(const PeAddParams& p, hipStream_t stream);
 hipError_t launch_gemm_bf16_ln(const GemmLnParams& p, hipStream_t stream);

@@ -30,6 +30,9 @@
 // rounded to bf16 for the products, and dQ, dK, dV once to bf16 at the store.
 
 #include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <mutex>
 #include <math.h>
 #include <stdint.h>
 
@@ -477,6 +480,36 @@ void sdpa_bwd_dq(const SdpaBwdParams p) {
 }
 
 }  // namespace
+
+// Fixed scratch of the allocation-free backward entry point: the lse2 and -D
+// planes, 8 bytes per query row of every (b, h), 2 M rows at most.  Each
+// device holds one copy for the life of the process and every call on that
+// device uses it.  In host code `scratch` only names the symbol: its device
+// address is looked up per device (hipGetSymbolAddress, with the device
+// current) and only that address is ever passed to a kernel.
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kBwdScratchBytes];
+
+hipError_t bwd_scratch(void** ptr) {
+  static std::atomic<void*> addr[kMaxDevices];
+  static std::mutex lock;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* a = addr[dev].load(std::memory_order_acquire);
+  if (!a) {
+    std::lock_guard<std::mutex> g(lock);
+    a = addr[dev].load(std::memory_order_relaxed);
+    if (!a) {
+      e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      addr[dev].store(a, std::memory_order_release);
+    }
+  }
+  *ptr = a;
+  return hipSuccess;
+}
 
 hipError_t launch_sdpa_bwd_bf16(const SdpaBwdParams& p, hipStream_t stream) {
   const int64_t bh = (int64_t)p.batch * p.heads;

@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 7
+#define ATTN_ABI_VERSION 8
 
 typedef void* attn_stream_t; /* hipStream_t */
 
@@ -329,6 +329,32 @@ int attn_sdpa_bwd(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_
                   const attn_strides* sdv, float scale, attn_mask mask, const int32_t* seqlens_q,
                   const int32_t* seqlens_kv, void* workspace, size_t workspace_bytes,
                   attn_stream_t stream);
+
+/*
+ * attn_sdpa_bwd_noalloc -- attn_sdpa_bwd without a workspace argument, for
+ * callers that cannot allocate device memory (code under graph capture, tight
+ * serving or training loops, harnesses that forbid allocation).
+ *
+ * Same arguments, results and errors as attn_sdpa_bwd, minus workspace and
+ * workspace_bytes.  The per-row terms it needs live in a fixed 16 MiB device
+ * array of the library instead, one per device, held until the process ends:
+ * batch * heads * n_q may be at most 2,097,152 (8 bytes per query row);
+ * larger calls return ATTN_E_WORKSPACE before anything is enqueued.  The
+ * array's address on the current device is looked up at the first call on
+ * that device (the current device must be the one `stream` belongs to; a
+ * failed lookup returns ATTN_E_HIP).  No call allocates or frees memory.
+ * Every call on one device uses the same array and overwrites what an earlier
+ * call left there before reading it: calls on one device whose kernels may
+ * run concurrently (different streams without ordering between them) race
+ * and must not be made; calls ordered on one stream are fine.
+ */
+int attn_sdpa_bwd_noalloc(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k, int d_v,
+                          const void* q, const attn_strides* sq, const void* k, const attn_strides* sk,
+                          const void* v, const attn_strides* sv, const void* o, const attn_strides* so,
+                          const void* dout, const attn_strides* sdo, const float* lse, void* dq,
+                          const attn_strides* sdq, void* dk, const attn_strides* sdk, void* dv,
+                          const attn_strides* sdv, float scale, attn_mask mask, const int32_t* seqlens_q,
+                          const int32_t* seqlens_kv, attn_stream_t stream);
 
 /* ATTN_ABI_VERSION of the loaded library. */
 int attn_abi_version(void);

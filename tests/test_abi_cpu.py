@@ -393,3 +393,20 @@ def test_binding_bwd_checks_gradients():
             attn.sdpa_bwd(q, k, k, q, lse, q, **{name: bad})
     with pytest.raises(ValueError, match="on the GPU"):
         attn.sdpa_bwd(q, k, k, q, lse, q)
+
+
+def test_bwd_noalloc_rejects_sizes_beyond_its_scratch():
+    """attn_sdpa_bwd_noalloc keeps its per-row terms in a fixed 16 MiB array
+    (8 bytes per query row): 2,097,152 rows of batch*heads*n_q at most.  One
+    row more is refused with ATTN_E_WORKSPACE before any HIP call (so this
+    runs without a GPU); argument errors come first, as in attn_sdpa_bwd."""
+    L = attn.lib()
+
+    def call(B, H, n_q, dt=1, lse=FAKE):
+        return L.attn_sdpa_bwd_noalloc(dt, B, H, n_q, 64, 64, 64, FAKE, None, FAKE, None, FAKE, None, FAKE, None,
+                                       FAKE, None, lse, FAKE, None, FAKE, None, FAKE, None, 0.0, 1, None, None,
+                                       None)
+    assert call(4, 16, 32769) == -4           # 2,097,216 rows
+    assert call(1, 1, 2097153) == -4
+    assert call(4, 16, 32769, dt=0) == -2     # f32: unsupported, as in attn_sdpa_bwd
+    assert call(4, 16, 32769, lse=None) == -1
