@@ -70,7 +70,7 @@ int check_sdpa(attn_dtype dt, int batch, int heads, int n_q, int n_kv, int d_k, 
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return ATTN_E_ALIGN;
     for (int t = 0; t < 4; ++t)
       if (!strides_aligned(out[t], 8)) return ATTN_E_ALIGN;
-    const int64_t qblocks = (n_q + 127) / 128;
+    const int64_t qblocks = ((int64_t)n_q + 127) / 128;
     if (qblocks * batch * heads > kMaxGrid) return ATTN_E_UNSUPPORTED;
     // Q/K/V rows are fetched through 32-bit buffer offsets from each (b, h)
     // slice, and rows past the lengths must fall outside the buffer range:

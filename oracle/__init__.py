@@ -24,6 +24,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# A differently built copy of oracle.c (the sanitizer tier loads one built
+# with -fsanitize=address,undefined); it is used as given, never rebuilt here.
+_LIB_OVERRIDE = os.environ.get("ATTN_ORACLE_LIB")
 _lib = None
 
 _D = ctypes.POINTER(ctypes.c_double)
@@ -45,9 +48,12 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-            build(force=True)
-        lib = ctypes.CDLL(_LIB_PATH)
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB_PATH)
         i, d = ctypes.c_int, ctypes.c_double
         lib.oracle_sdpa_f64.argtypes = [i, i, i, i, i, i, _D, _D, _D, _D, _D, d, i, _I, _I, i]
         lib.oracle_sdpa_rows_f64.argtypes = [i, i, i, i, i, i, _D, _D, _D, _L, ctypes.c_int64,
