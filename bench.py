@@ -151,9 +151,11 @@ def trials_info(per):
 
 def platform_info(torch):
     """The GPU, its architecture, the ROCm and HIP runtime versions, and the
-    shader clock that rocm-smi reports right after the timed region."""
+    shader clock right after the timed region, read from the device's sysfs
+    entries (the current DPM level of pp_dpm_sclk, else the hwmon sclk):
+    a process that has initialised the GPU starts no other program."""
+    import glob
     import re
-    import subprocess
     props = torch.cuda.get_device_properties(0)
     info = {"gpu": props.name, "arch": getattr(props, "gcnArchName", None),
             "compute_units": props.multi_processor_count, "hip_runtime": torch.version.hip}
@@ -164,16 +166,29 @@ def platform_info(torch):
         info["rocm"] = None
     sclk = None
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
-        for line in r.stdout.splitlines():
-            if "sclk" in line.lower():
-                m = re.search(r"(\d+)\s*[Mm]hz", line)
-                if m:
-                    sclk = int(m.group(1))
+        dev = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
+    except (AttributeError, TypeError):
+        dev = None
+    if dev is not None:
+        try:
+            with open(dev + "/pp_dpm_sclk") as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        m = re.search(r"(\d+)\s*[Mm]hz", line)
+                        if m:
+                            sclk = int(m.group(1))
+        except OSError:
+            pass
+        if sclk is None:
+            for path in sorted(glob.glob(dev + "/hwmon/hwmon*/freq1_input")):
+                try:
+                    with open(path) as f:
+                        sclk = int(f.read().strip()) // 1000000
                     break
-    except (OSError, subprocess.SubprocessError):
-        pass
+                except (OSError, ValueError):
+                    pass
     info["sclk_mhz_after_run"] = sclk
+    info["pci_device"] = dev.rsplit("/", 1)[-1] if dev else None
     return info
 
 
