@@ -45,7 +45,9 @@ METRIC = "attention fwd TFLOP/s (bf16) + % of MFMA peak, h=8 d_k=64 n=256 causal
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 CACHE_BYTES = 256 << 20       # Infinity Cache
-TIMING = "median of 5 replays of a HIP graph of the K timed steps, HIP events on the launch stream"
+SETTLE_S = 0.8                # untimed replays before the timed ones: the shader clock's ramp from idle
+TIMING = ("median of 5 replays of a HIP graph of the K timed steps, HIP events on the launch stream, "
+          "after 0.8 s of untimed replays of the same graph (the shader clock's ramp from idle)")
 # the forward kernel each short workload runs (one workgroup per (batch, head)
 # with the keys resident in LDS up to n_q 256 / n_kv 384)
 SDPA_KERNEL = {2: "sdpa_fwd_bf16_d64_resident", 3: "sdpa_fwd_bf16_d64_resident", 4: "sdpa_fwd_bf16_d64_resident"}
@@ -114,11 +116,71 @@ def to_dev(storage, dtype, dev):
 TRIALS = 5
 
 
-def time_graph(launches, K, W, torch, trials=TRIALS):
+# shader clock (MHz) sampled from sysfs at the end of the main measurement's
+# settling replays (filled by time_graph(..., clock=True))
+CLOCK_SAMPLES = []
+
+
+def sysfs_sclk_path(torch):
+    """The device's pp_dpm_sclk file (current DPM level marked with '*'), or None."""
+    try:
+        props = torch.cuda.get_device_properties(0)
+        path = "/sys/bus/pci/devices/%04x:%02x:%02x.0/pp_dpm_sclk" % (
+            props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
+    except (AttributeError, TypeError):
+        return None
+    return path if os.path.exists(path) else None
+
+
+def read_sclk(path):
+    import re
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    m = re.search(r"(\d+)\s*[Mm]hz", line)
+                    if m:
+                        return int(m.group(1))
+    except OSError:
+        pass
+    return None
+
+
+def settle_clock(g, stream, ms_per_replay, seconds, clock, torch):
+    """Replay the captured graph back to back, untimed, for about `seconds`:
+    from idle the shader clock takes 0.3-0.5 s of sustained load to reach its
+    steady state (measured: 870 MHz at the first replay, 2300 MHz after 0.3 s,
+    2395 MHz from 0.6 s on, on the decoder workload), and timing the first
+    milliseconds would measure the clock's ramp instead of the kernels.  With
+    clock=True the clock is read from sysfs (file reads only) during the last
+    0.1 s of the replays."""
+    import time
+    n = max(1, int(seconds * 1e3 / max(ms_per_replay, 1e-3)))
+    t0 = time.time()
+    with torch.cuda.stream(stream):
+        for _ in range(n):
+            g.replay()
+    path = sysfs_sclk_path(torch) if clock else None
+    if path is not None:
+        t_poll = t0 + max(0.0, n * ms_per_replay * 1e-3 - 0.15)
+        while time.time() < t_poll:
+            time.sleep(0.01)
+        t_end = time.time() + 0.1
+        while time.time() < t_end:
+            v = read_sclk(path)
+            if v is not None:
+                CLOCK_SAMPLES.append(v)
+            time.sleep(0.005)
+    torch.cuda.synchronize()
+
+
+def time_graph(launches, K, W, torch, trials=TRIALS, clock=False, settle_s=SETTLE_S):
     """Capture the K timed steps once in a graph, replay it once untimed after
-    W eager warmup steps, then time `trials` replays, each bracketed by HIP
-    events on the capture/launch stream.  Returns (median ms per step, the
-    per-replay ms per step, the graph)."""
+    W eager warmup steps, replay it untimed for settle_s seconds so that the
+    shader clock reaches its steady state, then time `trials` replays, each
+    bracketed by HIP events on the capture/launch stream.  Returns (median ms
+    per step, the per-replay ms per step, the graph).  With clock=True the
+    shader clock is sampled at the end of the settling replays."""
     for s in range(W):
         launches(s)
     torch.cuda.synchronize()
@@ -130,8 +192,13 @@ def time_graph(launches, K, W, torch, trials=TRIALS):
             for s in range(K):
                 launches(s)
     torch.cuda.synchronize()
-    g.replay()  # untimed: graph upload
-    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        g.replay()  # untimed: graph upload
+        e1.record(stream)
+    e1.synchronize()
+    settle_clock(g, stream, e0.elapsed_time(e1), settle_s, clock, torch)
     per = []
     for _ in range(trials):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -151,11 +218,9 @@ def trials_info(per):
 
 def platform_info(torch):
     """The GPU, its architecture, the ROCm and HIP runtime versions, and the
-    shader clock right after the timed region, read from the device's sysfs
-    entries (the current DPM level of pp_dpm_sclk, else the hwmon sclk):
-    a process that has initialised the GPU starts no other program."""
-    import glob
-    import re
+    shader clock sampled from the device's sysfs entry while the measured
+    graph replayed (a process that has initialised the GPU starts no other
+    program, so rocm-smi is not called)."""
     props = torch.cuda.get_device_properties(0)
     info = {"gpu": props.name, "arch": getattr(props, "gcnArchName", None),
             "compute_units": props.multi_processor_count, "hip_runtime": torch.version.hip}
@@ -164,31 +229,11 @@ def platform_info(torch):
             info["rocm"] = f.read().strip()
     except OSError:
         info["rocm"] = None
-    sclk = None
-    try:
-        dev = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
-    except (AttributeError, TypeError):
-        dev = None
-    if dev is not None:
-        try:
-            with open(dev + "/pp_dpm_sclk") as f:
-                for line in f:
-                    if line.rstrip().endswith("*"):
-                        m = re.search(r"(\d+)\s*[Mm]hz", line)
-                        if m:
-                            sclk = int(m.group(1))
-        except OSError:
-            pass
-        if sclk is None:
-            for path in sorted(glob.glob(dev + "/hwmon/hwmon*/freq1_input")):
-                try:
-                    with open(path) as f:
-                        sclk = int(f.read().strip()) // 1000000
-                    break
-                except (OSError, ValueError):
-                    pass
-    info["sclk_mhz_after_run"] = sclk
-    info["pci_device"] = dev.rsplit("/", 1)[-1] if dev else None
+    if CLOCK_SAMPLES:
+        v = sorted(CLOCK_SAMPLES)
+        info["sclk_mhz_under_load"] = {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "samples": len(v)}
+    else:
+        info["sclk_mhz_under_load"] = None
     return info
 
 
@@ -238,7 +283,7 @@ def bench_sdpa(cfg_id, K, W, args):
         if rc != 0:
             raise RuntimeError(f"attn_sdpa_fwd failed: {attn.status_str(rc)}")
 
-    ms, per, g = time_graph(launch, K, W, torch)
+    ms, per, g = time_graph(launch, K, W, torch, clock=True)
     # the graph replays must reproduce the eager result bit for bit
     ref = outs[0].clone()
     launch(0)
@@ -316,7 +361,7 @@ def bench_block(K, W, args):
                 raise RuntimeError(f"attn_mha_fwd failed: {attn.status_str(rc)}")
         return launch
 
-    ms, per, _ = time_graph(block_launcher(R), K, W, torch)
+    ms, per, _ = time_graph(block_launcher(R), K, W, torch, clock=True)
     ms_hot, _, _ = time_graph(block_launcher(1), K, W, torch)
     block_launcher(1)(0)   # y of input set 0 for the oracle comparison
     torch.cuda.synchronize()
@@ -439,7 +484,7 @@ def bench_window(K, W, args):
         if rc != 0:
             raise RuntimeError(f"attn_sdpa_window_fwd failed: {attn.status_str(rc)}")
 
-    ms, per, _ = time_graph(launch, K, W, torch)
+    ms, per, _ = time_graph(launch, K, W, torch, clock=True)
     sample_gpu = outs[0][:1, :4].double().cpu().numpy()
     pairs = B * H * sum(min(i, r) + 1 for i in range(n))
     flops = pairs * 256
@@ -494,7 +539,7 @@ def bench_decode(K, W, args):
         if rc != 0:
             raise RuntimeError(f"attn_decode_fwd failed: {attn.status_str(rc)}")
 
-    ms, per, _ = time_graph(launch, K, W, torch)
+    ms, per, _ = time_graph(launch, K, W, torch, clock=True)
     sample_gpu = outs[0].double().cpu().numpy()
     Lk = inp.seqlens_kv.astype(np.int64)
     pairs = int(H * sum(sum(max(0, min(int(l), int(l) - n_q + i + 1)) for i in range(n_q)) for l in Lk))
@@ -557,7 +602,7 @@ def bench_backward(K, W, args):
         if rc != 0:
             raise RuntimeError(f"attn_sdpa_bwd failed: {attn.status_str(rc)}")
 
-    ms, per, _ = time_graph(launch, K, W, torch)
+    ms, per, _ = time_graph(launch, K, W, torch, clock=True)
     sample_gpu = [t.double().cpu().numpy() for t in sets[0][6]]
     pairs = B * H * n * (n + 1) // 2
     flops = pairs * 10 * d
@@ -636,7 +681,7 @@ def bench_sublayer(K, W, args):
                 raise RuntimeError(f"attn_mha_fwd failed: {attn.status_str(rc)}")
         return launch
 
-    ms, per, _ = time_graph(block_launcher(R), K, W, torch)
+    ms, per, _ = time_graph(block_launcher(R), K, W, torch, clock=True)
     ms_hot, _, _ = time_graph(block_launcher(1), K, W, torch)
     ms_plain, _, _ = time_graph(plain_launcher(R), max(10, K), W, torch)
     ms_plain_hot, _, _ = time_graph(plain_launcher(1), max(10, K), W, torch)
