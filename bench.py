@@ -47,7 +47,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 CACHE_BYTES = 256 << 20       # Infinity Cache
 SETTLE_S = 0.8                # untimed replays before the timed ones: the shader clock's ramp from idle
 TIMING = ("median of 5 replays of a HIP graph of the K timed steps, HIP events on the launch stream, "
-          "after 0.8 s of untimed replays of the same graph (the shader clock's ramp from idle)")
+          "after {settle} s of untimed replays of the same graph (the shader clock's ramp from idle)")
 # the forward kernel each short workload runs (one workgroup per (batch, head)
 # with the keys resident in LDS up to n_q 256 / n_kv 384)
 SDPA_KERNEL = {2: "sdpa_fwd_bf16_d64_resident", 3: "sdpa_fwd_bf16_d64_resident", 4: "sdpa_fwd_bf16_d64_resident"}
@@ -155,6 +155,8 @@ def settle_clock(g, stream, ms_per_replay, seconds, clock, torch):
     clock=True the clock is read from sysfs (file reads only) during the last
     0.1 s of the replays."""
     import time
+    if seconds <= 0:
+        return
     n = max(1, int(seconds * 1e3 / max(ms_per_replay, 1e-3)))
     t0 = time.time()
     with torch.cuda.stream(stream):
@@ -174,7 +176,7 @@ def settle_clock(g, stream, ms_per_replay, seconds, clock, torch):
     torch.cuda.synchronize()
 
 
-def time_graph(launches, K, W, torch, trials=TRIALS, clock=False, settle_s=SETTLE_S):
+def time_graph(launches, K, W, torch, trials=TRIALS, clock=False, settle_s=None):
     """Capture the K timed steps once in a graph, replay it once untimed after
     W eager warmup steps, replay it untimed for settle_s seconds so that the
     shader clock reaches its steady state, then time `trials` replays, each
@@ -198,7 +200,7 @@ def time_graph(launches, K, W, torch, trials=TRIALS, clock=False, settle_s=SETTL
         g.replay()  # untimed: graph upload
         e1.record(stream)
     e1.synchronize()
-    settle_clock(g, stream, e0.elapsed_time(e1), settle_s, clock, torch)
+    settle_clock(g, stream, e0.elapsed_time(e1), SETTLE_S if settle_s is None else settle_s, clock, torch)
     per = []
     for _ in range(trials):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -313,7 +315,7 @@ def bench_sdpa(cfg_id, K, W, args):
                    "d_k": d_k, "d_v": d_v, "causal": inp.causal,
                    "key_lengths": None if inp.seqlens_kv is None else "per-sequence",
                    "cache": f"{'hot' if args.hot else 'cold'}: {R} rotating input sets of {per_set / 1e6:.1f} MB",
-                   "timing": TIMING, "trials": trials_info(per),
+                   "timing": TIMING.format(settle=SETTLE_S), "trials": trials_info(per),
                    "flops_per_step": flops, "algorithmic_bytes_per_step": algo_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / PEAK_HBM_GBS, "traffic": traffic,
@@ -434,7 +436,7 @@ def bench_block(K, W, args):
         "metric": "MHA block fwd TFLOP/s (bf16) + % of MFMA peak, X [4,4096,1024] h=16 causal",
         "value": tflops, "ms_per_step": ms, "pct_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "config": {"workload": inp.name, "batch": B, "n": n, "d_model": dm, "heads": h, "d_k": 64,
-                   "causal": True, "cache": mode, "timing": TIMING, "trials": trials_info(per),
+                   "causal": True, "cache": mode, "timing": TIMING.format(settle=SETTLE_S), "trials": trials_info(per),
                    "hot_ms_per_step": ms_hot, "hot_tflops": tf(flops, ms_hot),
                    "flops_per_step": flops,
                    "sdpa_ms": ms_sdpa, "sdpa_tflops": sdpa_tflops, "sdpa_trials": trials_info(per_sdpa),
@@ -497,7 +499,7 @@ def bench_window(K, W, args):
         "config": {"workload": inp.name, "batch": B, "heads": H, "n": n, "d_k": 64, "causal": True,
                    "window_radius": r,
                    "cache": f"{'hot' if args.hot else 'cold'}: {R} rotating input sets of {per_set / 1e6:.1f} MB",
-                   "timing": TIMING, "trials": trials_info(per),
+                   "timing": TIMING.format(settle=SETTLE_S), "trials": trials_info(per),
                    "flops_per_step": flops, "algorithmic_bytes_per_step": algo_bytes},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": read_traffic("window"),
@@ -553,7 +555,7 @@ def bench_decode(K, W, args):
         "config": {"workload": inp.name, "batch": B, "heads": H, "n_q": n_q, "cache_capacity": n_kv,
                    "cache_lengths": f"U{{1024..4096}}, sum {int(Lk.sum())}", "d_k": d_k,
                    "cache": f"{'hot' if args.hot else 'cold'}: {R} rotating input sets of {per_set / 1e6:.1f} MB",
-                   "timing": TIMING, "trials": trials_info(per),
+                   "timing": TIMING.format(settle=SETTLE_S), "trials": trials_info(per),
                    "flops_per_step": flops, "algorithmic_bytes_per_step": algo_bytes},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": read_traffic("decode"),
@@ -613,7 +615,7 @@ def bench_backward(K, W, args):
         "value": tflops, "ms_per_step": ms, "pct_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "config": {"workload": inp.name, "batch": B, "heads": H, "n": n, "d_k": d, "causal": True,
                    "cache": f"{'hot' if args.hot else 'cold'}: {R} rotating input sets of {per_set / 1e6:.1f} MB",
-                   "timing": TIMING, "trials": trials_info(per),
+                   "timing": TIMING.format(settle=SETTLE_S), "trials": trials_info(per),
                    "flops_per_step": flops, "flops_counted": "10*d per legal pair",
                    "algorithmic_bytes_per_step": algo_bytes},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -697,7 +699,7 @@ def bench_sublayer(K, W, args):
         "value": tflops, "ms_per_step": ms, "pct_mfma_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "config": {"workload": "sublayer_bf16_4x4096x1024_h16_causal_pe_ln", "batch": B, "n": n,
                    "d_model": dm, "heads": h, "d_k": 64, "causal": True, "add_pe": True, "ln_eps": 1e-5,
-                   "cache": mode, "timing": TIMING, "trials": trials_info(per),
+                   "cache": mode, "timing": TIMING.format(settle=SETTLE_S), "trials": trials_info(per),
                    "hot_ms_per_step": ms_hot, "hot_tflops": flops / (ms_hot * 1e-3) / 1e12,
                    "flops_per_step": flops, "flops_counted": "projections 2*M*N*K, attention 4*d per legal pair",
                    "block_without_pe_ln_ms": ms_plain, "block_without_pe_ln_hot_ms": ms_plain_hot},
@@ -797,6 +799,7 @@ def calibrate_copy(K):
 
 
 def main():
+    global SETTLE_S
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -804,9 +807,13 @@ def main():
     ap.add_argument("--workload", default="decoder", choices=sorted(WORKLOAD_CFG))
     ap.add_argument("--hot", action="store_true", help="reuse one input set (cache-hot)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle", type=float, default=SETTLE_S,
+                    help="seconds of untimed graph replays before each timed measurement (the shader clock's "
+                         "ramp from idle); 0 for counter passes, where every dispatch is instrumented")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a 256 MiB device copy instead (byte-counter calibration)")
     args = ap.parse_args()
+    SETTLE_S = max(0.0, args.settle)
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
