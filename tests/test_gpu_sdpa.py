@@ -131,6 +131,37 @@ def test_short_sequence_kernel_edges(case):
     check_against_oracle(inp, o, lse)
 
 
+def _sweep_cases(n=24, seed=2024):
+    """Seeded random shapes over both bf16 kernels and their limits: n_q and
+    n_kv up to 700 (the short-sequence kernel takes n_q <= 256, n_kv <= 384),
+    causal or not, lengths or not (including empty sequences), batch*heads
+    a multiple of 8 or not (the two workgroup orders)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        B, H = int(rng.integers(1, 4)), int(rng.choice([1, 2, 3, 8]))
+        nq = int(rng.choice([int(rng.integers(1, 257)), int(rng.integers(257, 701))]))
+        nkv = int(rng.choice([int(rng.integers(1, 385)), int(rng.integers(385, 701))]))
+        causal = bool(rng.integers(0, 2))
+        lq = [int(x) for x in rng.integers(0, nq + 1, size=B)] if rng.integers(0, 3) == 0 else None
+        lkv = [int(x) for x in rng.integers(0, nkv + 1, size=B)] if rng.integers(0, 2) == 0 else None
+        cases.append(dict(name=f"sweep{i:02d}_{B}x{H}x{nq}x{nkv}{'_causal' if causal else ''}"
+                               f"{'_lq' if lq else ''}{'_lkv' if lkv else ''}",
+                          B=B, H=H, nq=nq, nkv=nkv, causal=causal, lq=lq, lkv=lkv))
+    return cases
+
+
+SWEEP = _sweep_cases()
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=[c["name"] for c in SWEEP])
+def test_random_shape_sweep(case):
+    inp = _case(dtype="bf16", cfg_id=88, **case)
+    announce(f"sdpa {inp.name} shape={inp.shape} causal={inp.causal}")
+    o, lse = run_gpu(inp)
+    check_against_oracle(inp, o, lse)
+
+
 LONG = [
     # one head of 65,536 positions, causal: 1,024 key tiles, 8 MiB per operand
     dict(name="bf16_long_65536_causal", B=1, H=1, nq=65536, nkv=65536, causal=True),
