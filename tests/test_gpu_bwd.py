@@ -176,6 +176,34 @@ def test_bwd_vs_oracle(c):
     run_case(c.pop("name"), seed=seed, **c)
 
 
+def _bwd_sweep(n=10, seed=4242):
+    """Seeded random shapes: n_q and n_kv up to 520 (ragged against the
+    128-row blocks and 64-row tiles of both kernels), causal or not, query
+    and key lengths (zero included), batch*heads a multiple of 8 or not."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B, H = int(rng.integers(1, 3)), int(rng.choice([1, 2, 4]))
+        n_q, n_kv = int(rng.integers(1, 521)), int(rng.integers(1, 521))
+        causal = bool(rng.integers(0, 2))
+        lq = [int(x) for x in rng.integers(0, n_q + 1, size=B)] if rng.integers(0, 2) == 0 else None
+        lkv = [int(x) for x in rng.integers(0, n_kv + 1, size=B)] if rng.integers(0, 2) == 0 else None
+        out.append(dict(name=f"sweep{i:02d}_{B}x{H}x{n_q}x{n_kv}{'_causal' if causal else ''}"
+                             f"{'_lq' if lq else ''}{'_lkv' if lkv else ''}",
+                        B=B, H=H, n_q=n_q, n_kv=n_kv, causal=causal, lq=lq, lkv=lkv))
+    return out
+
+
+BWD_SWEEP = _bwd_sweep()
+
+
+@pytest.mark.parametrize("c", BWD_SWEEP, ids=[c["name"] for c in BWD_SWEEP])
+def test_bwd_random_shape_sweep(c):
+    seed = 500 + BWD_SWEEP.index(c)
+    c = dict(c)
+    run_case(c.pop("name"), seed=seed, **c)
+
+
 def test_bwd_zero_dout_gives_zero_gradients():
     """dO = 0 makes dV = P^T 0 and dS = P (0 - 0) vanish: every gradient is
     exactly zero."""
