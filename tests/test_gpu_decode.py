@@ -76,6 +76,34 @@ def test_decode_vs_oracle(c):
     compare(inp, o, lse, name)
 
 
+def _decode_sweep(n=10, seed=77):
+    """Seeded random decoding steps: 1-32 new queries, caches up to 6000 rows
+    (one chunk up to the split over workgroups), lengths from 0 to the
+    capacity, batch*heads from 1 to 96."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B, H = int(rng.integers(1, 7)), int(rng.integers(1, 17))
+        n_q = int(rng.choice([1, 1, 2, 4, 7, 16, 32]))
+        n_kv = int(rng.integers(1, 6001))
+        L = [int(x) for x in rng.integers(0, n_kv + 1, size=B)]
+        out.append(dict(name=f"sweep{i:02d}_{B}x{H}_q{n_q}_cache{n_kv}", B=B, H=H, n_q=n_q, n_kv=n_kv, L=L))
+    return out
+
+
+DECODE_SWEEP = _decode_sweep()
+
+
+@pytest.mark.parametrize("c", DECODE_SWEEP, ids=[c["name"] for c in DECODE_SWEEP])
+def test_decode_random_shape_sweep(c):
+    c = dict(c)
+    name = c.pop("name")
+    inp = gen.decode_workload(**c)
+    announce(f"decode {name} {inp.shape} L={inp.seqlens_kv.tolist()}")
+    o, lse = run(inp)
+    compare(inp, o, lse, name)
+
+
 def test_decode_strided_cache():
     inp = gen.decode_workload(B=2, H=3, n_q=3, n_kv=700, lo=200)
     announce(f"decode strided cache {inp.shape}")

@@ -63,6 +63,34 @@ def test_window_bf16_vs_oracle(c):
     run_case(c.pop("name"), "bf16", seed=len(CASES), **c)
 
 
+def _window_sweep(n=10, seed=91):
+    """Seeded random restricted-attention shapes: n_q, n_kv up to 800, radius
+    0 to 400, causal or not, lengths or not."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        n_q, n_kv = int(rng.integers(1, 801)), int(rng.integers(1, 801))
+        r = int(rng.choice([0, 1, int(rng.integers(2, 65)), int(rng.integers(65, 401))]))
+        causal = bool(rng.integers(0, 2))
+        lq = [int(x) for x in rng.integers(0, n_q + 1, size=B)] if rng.integers(0, 3) == 0 else None
+        lkv = [int(x) for x in rng.integers(0, n_kv + 1, size=B)] if rng.integers(0, 2) == 0 else None
+        out.append(dict(name=f"sweep{i:02d}_{B}x{H}x{n_q}x{n_kv}_r{r}{'_causal' if causal else ''}"
+                             f"{'_lq' if lq else ''}{'_lkv' if lkv else ''}",
+                        B=B, H=H, n_q=n_q, n_kv=n_kv, r=r, causal=causal, lq=lq, lkv=lkv))
+    return out
+
+
+WINDOW_SWEEP = _window_sweep()
+
+
+@pytest.mark.parametrize("c", WINDOW_SWEEP, ids=[c["name"] for c in WINDOW_SWEEP])
+def test_window_random_shape_sweep(c):
+    seed = 40 + WINDOW_SWEEP.index(c)
+    c = dict(c)
+    run_case(c.pop("name"), "bf16", seed=seed, **c)
+
+
 def test_window_zero_returns_v():
     """r = 0: every query attends to itself only, so O = V exactly (the weight
     is 1 and V is already bf16)."""
