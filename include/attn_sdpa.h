@@ -161,6 +161,9 @@ size_t attn_mha_workspace_bytes(attn_dtype dt, int batch, int n_q, int n_kv, int
  *             head h's output column c)
  *   y         [batch, n_q, d_model] bf16, written in full
  *   dt        ATTN_BF16 only; d_k = d_v = 64; d_model a multiple of 64.
+ *   heads     d_model / d_k: the heads split d_model (d_k = d_v = d_model/h,
+ *             section 3.2.2); heads*d_k != d_model or heads*d_v != d_model
+ *             is ATTN_E_INVALID.
  *   scale, mask, seqlens_q, seqlens_kv: as in attn_sdpa_fwd (padded query
  *             rows give zero rows of y).
  *   workspace device memory of at least attn_mha_workspace_bytes(...) bytes,
@@ -272,7 +275,8 @@ size_t attn_mha_block_workspace_bytes(attn_dtype dt, int batch, int n_q, int n_k
  *   x_q [batch, n_q, d_model], x_kv [batch, n_kv, d_model] (may be NULL when
  *   n_kv = 0), y [batch, n_q, d_model]; w_* as for attn_mha_fwd; ln_gamma,
  *   ln_beta [d_model]; all bf16, contiguous, 16-byte aligned.  dt = ATTN_BF16, d_k = d_v = 64,
- *   d_model in {256, 512, 768, 1024} (otherwise ATTN_E_UNSUPPORTED).
+ *   d_model in {256, 512, 768, 1024} (otherwise ATTN_E_UNSUPPORTED), heads*d_k =
+ *   heads*d_v = d_model (otherwise ATTN_E_INVALID).
  *   add_pe is 0 or 1 and needs x_kv == x_q (and then n_kv == n_q); ln_eps
  *   finite and > 0; scale, mask and the lengths as for attn_mha_fwd (rows
  *   i >= L_q get the attention output 0, so their y is LayerNorm(h)).
