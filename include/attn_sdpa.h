@@ -58,8 +58,10 @@
  *     Nothing is printed.  Asynchronous device faults surface at the caller's
  *     next synchronisation.
  *   - Lengths arrays are device int32 [batch]; values are clamped to [0, n].
- *   - Thread safety: calls may be made from several host threads; the library
- *     keeps only a lazily initialised per-device properties cache.
+ *   - Thread safety: calls may be made from several host threads.  The
+ *     library's only host state is the per-thread value behind
+ *     attn_last_hip_error and, for attn_sdpa_bwd_noalloc, the per-device
+ *     address of its scratch array, looked up once under a lock.
  */
 #ifndef ATTN_SDPA_H
 #define ATTN_SDPA_H
