@@ -192,8 +192,9 @@ def test_scale_brings_score_variance_to_one():
     d = 64
     q, k = rnd(19, (1, 4, 64, d)), rnd(20, (1, 4, 64, d))
     P, lse = weights_via_identity(q, k)
-    S = np.log(P) + lse[..., None]
-    assert abs(S.var() - 1.0) < 0.1
+    with np.errstate(divide="ignore", invalid="ignore"):   # a planted mistake may zero weights
+        S = np.log(P) + lse[..., None]
+        assert abs(S.var() - 1.0) < 0.1
     raw = q @ np.swapaxes(k, -1, -2)
     assert abs(np.abs(S * math.sqrt(d) - raw).max()) < 1e-10
 
