@@ -176,13 +176,10 @@ def settle_clock(g, stream, ms_per_replay, seconds, clock, torch):
     torch.cuda.synchronize()
 
 
-def time_graph(launches, K, W, torch, trials=TRIALS, clock=False, settle_s=None):
-    """Capture the K timed steps once in a graph, replay it once untimed after
-    W eager warmup steps, replay it untimed for settle_s seconds so that the
-    shader clock reaches its steady state, then time `trials` replays, each
-    bracketed by HIP events on the capture/launch stream.  Returns (median ms
-    per step, the per-replay ms per step, the graph).  With clock=True the
-    shader clock is sampled at the end of the settling replays."""
+def capture_graph(launches, K, W, torch):
+    """W eager warmup steps, then the K steps captured once in a graph on a
+    stream of its own and replayed once untimed (graph upload).  Returns the
+    graph, its stream and the upload replay's ms."""
     for s in range(W):
         launches(s)
     torch.cuda.synchronize()
@@ -200,7 +197,12 @@ def time_graph(launches, K, W, torch, trials=TRIALS, clock=False, settle_s=None)
         g.replay()  # untimed: graph upload
         e1.record(stream)
     e1.synchronize()
-    settle_clock(g, stream, e0.elapsed_time(e1), SETTLE_S if settle_s is None else settle_s, clock, torch)
+    return g, stream, e0.elapsed_time(e1)
+
+
+def replay_trials(g, stream, K, trials, torch):
+    """ms per step of `trials` replays, each bracketed by HIP events on the
+    graph's stream."""
     per = []
     for _ in range(trials):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -210,9 +212,45 @@ def time_graph(launches, K, W, torch, trials=TRIALS, clock=False, settle_s=None)
             e1.record(stream)
         e1.synchronize()
         per.append(e0.elapsed_time(e1) / K)
-    torch.cuda.synchronize()
-    return float(np.median(per)), per, g
+    return per
 
+
+def time_graph(launches, K, W, torch, trials=TRIALS, clock=False, settle_s=None, then=None):
+    """Capture the K timed steps once in a graph, replay it once untimed after
+    W eager warmup steps, replay it untimed for settle_s seconds so that the
+    shader clock reaches its steady state, then time `trials` replays, each
+    bracketed by HIP events on the capture/launch stream.  Returns (median ms
+    per step, the per-replay ms per step, the graph).  With clock=True the
+    shader clock is sampled at the end of the settling replays.  `then`, a
+    second step function, is captured before the settling replays and timed
+    right after the first one's trials (no idle gap between them); its
+    (median, per-replay) pair is then returned as a fourth element."""
+    g, stream, ms_upload = capture_graph(launches, K, W, torch)
+    g2 = capture_graph(then, K, W, torch) if then is not None else None
+    settle_clock(g, stream, ms_upload, SETTLE_S if settle_s is None else settle_s, clock, torch)
+    per = replay_trials(g, stream, K, trials, torch)
+    per2 = replay_trials(g2[0], g2[1], K, trials, torch) if g2 is not None else None
+    torch.cuda.synchronize()
+    if g2 is None:
+        return float(np.median(per)), per, g
+    return float(np.median(per)), per, g, (float(np.median(per2)), per2)
+
+def hot_context(hot, args, flops=None, algo_bytes=None):
+    """The same step on one input set at every launch (its bytes then stay in
+    L2 and the Infinity Cache), timed right after the cold trials from a graph
+    captured before them: context beside the cold value, never the value.
+    Empty when the whole run is already hot."""
+    if args.hot or hot is None:
+        return {}
+    ms_hot, per_hot = hot
+    out = {"hot_ms_per_step": ms_hot, "hot_trials": trials_info(per_hot),
+           "hot_note": "one input set at every launch (cache-resident), timed right after the cold "
+                       "replays; context, not the value"}
+    if flops:
+        out["hot_tflops"] = flops / (ms_hot * 1e-3) / 1e12
+    if algo_bytes:
+        out["hot_gbs_algorithmic"] = algo_bytes / (ms_hot * 1e-3) / 1e9
+    return out
 
 def trials_info(per):
     return {"replays": len(per), "min_ms": min(per), "median_ms": float(np.median(per)), "max_ms": max(per)}
@@ -285,7 +323,9 @@ def bench_sdpa(cfg_id, K, W, args):
         if rc != 0:
             raise RuntimeError(f"attn_sdpa_fwd failed: {attn.status_str(rc)}")
 
-    ms, per, g = time_graph(launch, K, W, torch, clock=True)
+    timed = time_graph(launch, K, W, torch, clock=True,
+                       then=None if args.hot else (lambda s: launch(0)))
+    ms, per, hot = timed[0], timed[1], (timed[3] if len(timed) > 3 else None)
     # the graph replays must reproduce the eager result bit for bit
     ref = outs[0].clone()
     launch(0)
@@ -316,7 +356,8 @@ def bench_sdpa(cfg_id, K, W, args):
                    "key_lengths": None if inp.seqlens_kv is None else "per-sequence",
                    "cache": f"{'hot' if args.hot else 'cold'}: {R} rotating input sets of {per_set / 1e6:.1f} MB",
                    "timing": TIMING.format(settle=SETTLE_S), "trials": trials_info(per),
-                   "flops_per_step": flops, "algorithmic_bytes_per_step": algo_bytes},
+                   "flops_per_step": flops, "algorithmic_bytes_per_step": algo_bytes,
+                   **hot_context(hot, args, flops, algo_bytes)},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": SDPA_KERNEL[cfg_id], "algorithmic_bytes_per_launch": algo_bytes},
@@ -486,7 +527,9 @@ def bench_window(K, W, args):
         if rc != 0:
             raise RuntimeError(f"attn_sdpa_window_fwd failed: {attn.status_str(rc)}")
 
-    ms, per, _ = time_graph(launch, K, W, torch, clock=True)
+    timed = time_graph(launch, K, W, torch, clock=True,
+                       then=None if args.hot else (lambda s: launch(0)))
+    ms, per, hot = timed[0], timed[1], (timed[3] if len(timed) > 3 else None)
     sample_gpu = outs[0][:1, :4].double().cpu().numpy()
     pairs = B * H * sum(min(i, r) + 1 for i in range(n))
     flops = pairs * 256
@@ -500,7 +543,8 @@ def bench_window(K, W, args):
                    "window_radius": r,
                    "cache": f"{'hot' if args.hot else 'cold'}: {R} rotating input sets of {per_set / 1e6:.1f} MB",
                    "timing": TIMING.format(settle=SETTLE_S), "trials": trials_info(per),
-                   "flops_per_step": flops, "algorithmic_bytes_per_step": algo_bytes},
+                   "flops_per_step": flops, "algorithmic_bytes_per_step": algo_bytes,
+                   **hot_context(hot, args, flops, algo_bytes)},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": read_traffic("window"),
                      "kernel": "sdpa_fwd_bf16_d64 (band)", "algorithmic_bytes_per_launch": algo_bytes,
@@ -541,7 +585,9 @@ def bench_decode(K, W, args):
         if rc != 0:
             raise RuntimeError(f"attn_decode_fwd failed: {attn.status_str(rc)}")
 
-    ms, per, _ = time_graph(launch, K, W, torch, clock=True)
+    timed = time_graph(launch, K, W, torch, clock=True,
+                       then=None if args.hot else (lambda s: launch(0)))
+    ms, per, hot = timed[0], timed[1], (timed[3] if len(timed) > 3 else None)
     sample_gpu = outs[0].double().cpu().numpy()
     Lk = inp.seqlens_kv.astype(np.int64)
     pairs = int(H * sum(sum(max(0, min(int(l), int(l) - n_q + i + 1)) for i in range(n_q)) for l in Lk))
@@ -556,7 +602,8 @@ def bench_decode(K, W, args):
                    "cache_lengths": f"U{{1024..4096}}, sum {int(Lk.sum())}", "d_k": d_k,
                    "cache": f"{'hot' if args.hot else 'cold'}: {R} rotating input sets of {per_set / 1e6:.1f} MB",
                    "timing": TIMING.format(settle=SETTLE_S), "trials": trials_info(per),
-                   "flops_per_step": flops, "algorithmic_bytes_per_step": algo_bytes},
+                   "flops_per_step": flops, "algorithmic_bytes_per_step": algo_bytes,
+                   **hot_context(hot, args, flops, algo_bytes)},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": read_traffic("decode"),
                      "kernel": "sdpa_decode_partial_bf16 (at this size the chunks of a (b, h) merge in the workgroup: no combine kernel)",
@@ -604,7 +651,9 @@ def bench_backward(K, W, args):
         if rc != 0:
             raise RuntimeError(f"attn_sdpa_bwd failed: {attn.status_str(rc)}")
 
-    ms, per, _ = time_graph(launch, K, W, torch, clock=True)
+    timed = time_graph(launch, K, W, torch, clock=True,
+                       then=None if args.hot else (lambda s: launch(0)))
+    ms, per, hot = timed[0], timed[1], (timed[3] if len(timed) > 3 else None)
     sample_gpu = [t.double().cpu().numpy() for t in sets[0][6]]
     pairs = B * H * n * (n + 1) // 2
     flops = pairs * 10 * d
@@ -617,7 +666,8 @@ def bench_backward(K, W, args):
                    "cache": f"{'hot' if args.hot else 'cold'}: {R} rotating input sets of {per_set / 1e6:.1f} MB",
                    "timing": TIMING.format(settle=SETTLE_S), "trials": trials_info(per),
                    "flops_per_step": flops, "flops_counted": "10*d per legal pair",
-                   "algorithmic_bytes_per_step": algo_bytes},
+                   "algorithmic_bytes_per_step": algo_bytes,
+                   **hot_context(hot, args, flops)},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / PEAK_BF16_TFLOPS, "traffic": read_traffic("backward"),
                      "kernel": "attn_sdpa_bwd (sdpa_bwd_dq, then sdpa_bwd_dkdv), timed as one call",
