@@ -100,3 +100,14 @@ def test_no_gpu_is_an_error():
     r = run_bench("--steps", "1", "--warmup", "0")
     assert r.returncode == 1
     assert "needs a GPU" in r.stderr
+
+
+def test_hot_context_is_context_only():
+    import types
+    cold = types.SimpleNamespace(hot=False)
+    assert bench.hot_context(None, cold) == {}
+    assert bench.hot_context((0.008, [0.008, 0.009]), types.SimpleNamespace(hot=True)) == {}
+    out = bench.hot_context((0.008, [0.008, 0.009, 0.007]), cold, flops=2e9, algo_bytes=32e6)
+    assert out["hot_ms_per_step"] == 0.008
+    assert abs(out["hot_tflops"] - 250.0) < 1e-9 and abs(out["hot_gbs_algorithmic"] - 4000.0) < 1e-9
+    assert out["hot_trials"]["median_ms"] == 0.008 and "value" not in out
