@@ -107,3 +107,36 @@ def test_block_full_size_every_row():
     causal, with the encoding, in the launch configuration the benchmark
     times: every output row checked against the oracle's whole sublayer."""
     run("full_4x4096x1024", 4, 4096, 4096, 1024, 16, True, True, seed=9)
+
+
+@pytest.mark.parametrize("dm,heads", [(256, 4), (1024, 16)])
+def test_constant_rows_give_beta_exactly(dm, heads):
+    """The degenerate case of LayerNorm: with W^O = 0 the attention output is
+    exactly 0, so z = h; with every row of x constant (and no positional
+    encoding) z - mean(z) is exactly 0 (d_model a power of two: the row sum
+    of a bf16 value and the division by d_model are exact in fp32), the
+    variance is 0, and y = gamma * 0 / sqrt(eps) + beta = beta, bit for bit,
+    padded query rows included."""
+    import torch
+    attn = attn_mod()
+    B, n = 2, 200
+    announce(f"block constant rows d_model={dm} heads={heads}")
+    rng = np.random.default_rng(4321 + dm)
+    c = gen.to_dtype(rng.standard_normal((B, n, 1)) * 3.0, "bf16")
+    x = np.broadcast_to(c, (B, n, dm)).copy()
+    hd = heads * 64
+    ws = [gen.to_dtype(gen.xavier_uniform(60 + t, *shape), "bf16") for t, shape in enumerate([(dm, hd)] * 3)]
+    ws.append(np.zeros((hd, dm)))
+    g = gen.to_dtype(1.0 + 0.1 * rng.standard_normal(dm), "bf16")
+    b = gen.to_dtype(0.5 * rng.standard_normal(dm), "bf16")
+    xg = to_gpu(gen.bf16_bits(x), "bf16")
+    wg = [to_gpu(gen.bf16_bits(w), "bf16") for w in ws]
+    gg, bg = to_gpu(gen.bf16_bits(g), "bf16"), to_gpu(gen.bf16_bits(b), "bf16")
+    y = attn.mha_block(xg, *wg, gg, bg, heads=heads, add_pe=False, ln_eps=1e-5, causal=True,
+                       seqlens_q=lens_gpu(np.array([n, 137], np.int32)),
+                       seqlens_kv=lens_gpu(np.array([n, 137], np.int32)))
+    torch.cuda.synchronize()
+    want = bg.view(torch.int16).expand(B, n, dm)
+    same = y.view(torch.int16) == want
+    print(f"constant rows d_model={dm}: {int(same.sum())} of {same.numel()} elements equal beta", flush=True)
+    assert bool(same.all())
