@@ -88,3 +88,43 @@ def test_zero_queries_decode_step():
     torch.cuda.synchronize()
     # query i of sequence b sits at position Lk[b] - n_q + i and sees keys up to it
     check(to_f64(o), v, True, None, Lk, shift=Lk - n_q, what="decoding step")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_zero_queries_backward(causal):
+    """Gradients with Q = 0: the weights of query i are 1/n_i over its n_i
+    legal keys, so dK = scale dS^T Q is exactly zero and dV_j = sum over the
+    queries i that may use key j of dO_i / n_i.  Bound for dV: the weights
+    are recomputed from the forward's lse and rounded to bf16 for the product
+    (relative 2^-8 each), plus one bf16 rounding of dV."""
+    import torch
+    attn = attn_mod()
+    announce(f"uniform weights: backward causal={causal}")
+    B, H, n = 2, 2, 300
+    k = gen.to_dtype(gen.normal(1201, (B, H, n, 64)), "bf16")
+    v = gen.to_dtype(gen.normal(1202, (B, H, n, 64)), "bf16")
+    do = gen.to_dtype(gen.normal(1203, (B, H, n, 64)), "bf16")
+    L = np.array([300, 211], np.int32)
+    qg = to_gpu(gen.bf16_bits(np.zeros((B, H, n, 64))), "bf16")
+    kg, vg, dog = (to_gpu(gen.bf16_bits(a), "bf16") for a in (k, v, do))
+    o, lse = attn.sdpa(qg, kg, vg, causal=causal, seqlens_q=lens_gpu(L), seqlens_kv=lens_gpu(L), return_lse=True)
+    dq, dk, dv = attn.sdpa_bwd(qg, kg, vg, o, lse, dog, causal=causal, seqlens_q=lens_gpu(L),
+                               seqlens_kv=lens_gpu(L))
+    torch.cuda.synchronize()
+    assert bool((dk.float() == 0).all()), "dK must be exactly zero when Q = 0"
+    dv = to_f64(dv)
+    worst = 0.0
+    for b in range(B):
+        for j in range(n):
+            users = [i for i in range(L[b]) if j < L[b] and (not causal or j <= i)]
+            if not users:
+                assert np.all(dv[b, :, j] == 0.0)
+                continue
+            cnt = np.array([(i + 1) if causal else L[b] for i in users], dtype=np.float64)
+            terms = do[b][:, users] / cnt[None, :, None]          # [H, users, d]
+            want = terms.sum(axis=1)
+            tol = 2.0 ** -7 * np.abs(terms).sum(axis=1) + 2.0 ** -8 * np.abs(want) + 1e-6
+            ratio = float((np.abs(dv[b, :, j] - want) / tol).max())
+            worst = max(worst, ratio)
+            assert ratio <= 1.0, f"dV row {b},{j}: error/bound {ratio:.3f}"
+    print(f"backward causal={causal}: dK exactly 0, dV max error/bound {worst:.3f}", flush=True)
