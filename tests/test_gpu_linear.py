@@ -111,3 +111,21 @@ def test_linear_empty():
     w = torch.zeros((64, 8), dtype=torch.bfloat16, device="cuda:0")
     y = attn.linear(x, w)
     assert y.shape == (0, 8)
+
+
+@pytest.mark.parametrize("M,K,N", [(300, 256, 512), (256, 1024, 256), (77, 64, 200)])
+def test_one_hot_rows_select_weight_rows_exactly(M, K, N):
+    """x with one 1 per row (row i selects weight row (7 i) mod K): every
+    product but one is an exact zero and the sum is that weight entry, so y
+    equals the selected rows of W bit for bit, on both GEMM kernels."""
+    import torch
+    attn = attn_mod()
+    announce(f"linear one-hot rows M={M} K={K} N={N}")
+    sel = (7 * np.arange(M)) % K
+    x = np.zeros((M, K))
+    x[np.arange(M), sel] = 1.0
+    w = gen.to_dtype(gen.xavier_uniform(7100 + N, K, N) * 3.0, "bf16")
+    wg = to_gpu(gen.bf16_bits(w), "bf16")
+    y = attn.linear(to_gpu(gen.bf16_bits(x), "bf16"), wg)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), wg[torch.from_numpy(sel).to(wg.device)].view(torch.int16))
